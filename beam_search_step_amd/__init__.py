@@ -1,0 +1,309 @@
+"""Python binding of libbeamstep.so (the C ABI in include/beamstep.h).
+
+Argument marshalling only: every step of the beam search runs in the HIP
+kernels of the library. torch tensors supply device memory and the HIP stream
+(``data_ptr()`` and ``torch.cuda.current_stream().cuda_stream``). The library
+must have been built (``__graft_entry__.build()``); importing the binding
+without it raises, and there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbeamstep.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "beamstep.h")
+
+BS_OK, BS_EINVAL, BS_ENOMEM, BS_EDEVICE, BS_ESTATE = 0, -1, -2, -3, -4
+BS_F32, BS_BF16 = 0, 1
+BS_LP_NONE, BS_LP_GNMT, BS_LP_POW = 0, 1, 2
+BS_STOP_TRUE, BS_STOP_HEURISTIC, BS_STOP_NEVER = 0, 1, 2
+
+DTYPES = {"f32": BS_F32, "bf16": BS_BF16}
+LPS = {"none": BS_LP_NONE, "gnmt": BS_LP_GNMT, "pow": BS_LP_POW}
+STOPS = {"true": BS_STOP_TRUE, "heuristic": BS_STOP_HEURISTIC, "never": BS_STOP_NEVER}
+
+
+class bs_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("beam", ctypes.c_int32), ("vocab", ctypes.c_int32),
+        ("max_steps", ctypes.c_int32), ("eos_id", ctypes.c_int32), ("pad_id", ctypes.c_int32),
+        ("logits_dtype", ctypes.c_int32), ("lp", ctypes.c_int32), ("alpha", ctypes.c_double),
+        ("stop", ctypes.c_int32), ("num_return", ctypes.c_int32), ("tile_elems", ctypes.c_int32),
+    ]
+
+
+class bs_kv_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_planes", ctypes.c_int32), ("planes", ctypes.POINTER(ctypes.c_void_p)),
+        ("row_stride", ctypes.c_int64), ("pos_stride", ctypes.c_int64),
+        ("pos_offset", ctypes.c_int64), ("bytes_per_pos", ctypes.c_int64),
+    ]
+
+
+class BeamStepError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {bs_strerror(status)} ({status})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libbeamstep.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.bs_strerror.restype = ctypes.c_char_p
+        L.bs_strerror.argtypes = [ctypes.c_int]
+        L.bs_create.argtypes = [ctypes.POINTER(bs_config), P, ctypes.POINTER(P)]
+        L.bs_reset.argtypes = [P]
+        L.bs_step.argtypes = [P, P, i64, P, P, P, P]
+        L.bs_reorder_kv.argtypes = [P, ctypes.POINTER(bs_kv_desc), i32]
+        L.bs_finalize.argtypes = [P, P, P, P]
+        L.bs_last_selection.argtypes = [P, P, P]
+        L.bs_get_finished.argtypes = [P, P, P, P, P, P, P]
+        L.bs_steps_taken.argtypes = [P]
+        L.bs_destroy.argtypes = [P]
+        L.bs_destroy.restype = None
+        L.bs_verify_create.argtypes = [i32, i32, i32, i32, P, ctypes.POINTER(P)]
+        L.bs_verify.argtypes = [P, P, i64, P, P, P]
+        L.bs_verify_destroy.argtypes = [P]
+        L.bs_verify_destroy.restype = None
+        for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_finalize",
+                     "bs_last_selection", "bs_get_finished", "bs_steps_taken",
+                     "bs_verify_create", "bs_verify"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/beamstep.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bs_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int, call: str) -> None:
+    if status != BS_OK:
+        raise BeamStepError(status, call)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one function each
+# ---------------------------------------------------------------------------
+
+def bs_strerror(status: int) -> str:
+    return library().bs_strerror(status).decode()
+
+
+def bs_create(cfg: bs_config, stream=None) -> int:
+    h = ctypes.c_void_p()
+    _check(library().bs_create(ctypes.byref(cfg), _stream(stream), ctypes.byref(h)), "bs_create")
+    return h.value
+
+
+def bs_reset(h: int) -> None:
+    _check(library().bs_reset(h), "bs_reset")
+
+
+def bs_step(h: int, logits, beam_idx, token_id, scores, done) -> None:
+    stride = logits.stride(0) if logits.dim() == 2 else logits.shape[-1]
+    _check(library().bs_step(h, _ptr(logits), stride, _ptr(beam_idx), _ptr(token_id),
+                             _ptr(scores), _ptr(done)), "bs_step")
+
+
+def make_kv_desc(planes: Sequence, pos_offset: int = 0) -> bs_kv_desc:
+    """Descriptor of planes that are torch tensors [rows, positions, ...]."""
+    p0 = planes[0]
+    es = p0.element_size()
+    arr = (ctypes.c_void_p * len(planes))(*[p.data_ptr() for p in planes])
+    d = bs_kv_desc(len(planes), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                   p0.stride(0) * es, p0.stride(1) * es, pos_offset,
+                   p0[0, 0].numel() * es)
+    d._keep = arr  # the pointer array must outlive the call
+    return d
+
+
+def bs_reorder_kv(h: int, kv: bs_kv_desc, gen_len: int) -> None:
+    _check(library().bs_reorder_kv(h, ctypes.byref(kv), gen_len), "bs_reorder_kv")
+
+
+def bs_finalize(h: int, tokens, lengths, norm_scores) -> None:
+    _check(library().bs_finalize(h, _ptr(tokens), _ptr(lengths), _ptr(norm_scores)),
+           "bs_finalize")
+
+
+def bs_last_selection(h: int, flat_idx, cand_score) -> None:
+    _check(library().bs_last_selection(h, _ptr(flat_idx), _ptr(cand_score)),
+           "bs_last_selection")
+
+
+def bs_get_finished(h: int, norm, raw, length, step, rank, count) -> None:
+    _check(library().bs_get_finished(h, _ptr(norm), _ptr(raw), _ptr(length), _ptr(step),
+                                     _ptr(rank), _ptr(count)), "bs_get_finished")
+
+
+def bs_steps_taken(h: int) -> int:
+    return library().bs_steps_taken(h)
+
+
+def bs_destroy(h: int) -> None:
+    library().bs_destroy(h)
+
+
+def bs_verify_create(batch: int, k: int, vocab: int, dtype: int, stream=None) -> int:
+    h = ctypes.c_void_p()
+    _check(library().bs_verify_create(batch, k, vocab, dtype, _stream(stream), ctypes.byref(h)),
+           "bs_verify_create")
+    return h.value
+
+
+def bs_verify(h: int, logits, proposals, accept_len, argmax) -> None:
+    stride = logits.shape[-1] if logits.dim() == 3 else logits.stride(0)
+    _check(library().bs_verify(h, _ptr(logits), stride, _ptr(proposals), _ptr(accept_len),
+                               _ptr(argmax)), "bs_verify")
+
+
+def bs_verify_destroy(h: int) -> None:
+    library().bs_verify_destroy(h)
+
+
+# ---------------------------------------------------------------------------
+# convenience wrapper owning the handle and the output tensors
+# ---------------------------------------------------------------------------
+
+class BeamSearch:
+    """One batched beam search on the current GPU.
+
+    ``step(logits)`` runs expand/score/prune/finalize; ``reorder_kv(planes,
+    gen_len)`` moves the KV cache rows that changed parent; ``finalize()``
+    returns the best hypotheses. Outputs are torch tensors on the device.
+    """
+
+    def __init__(self, batch, beam, vocab, max_steps, eos_id=-1, pad_id=-1, dtype="f32",
+                 lp="gnmt", alpha=0.6, stop="heuristic", num_return=1, tile_elems=0,
+                 stream=None):
+        import torch
+        self.B, self.W, self.V, self.T = batch, beam, vocab, max_steps
+        self.num_return = num_return
+        self.cfg = bs_config(batch, beam, vocab, max_steps, eos_id, pad_id, DTYPES[dtype],
+                             LPS[lp], float(alpha), STOPS[stop], num_return, tile_elems)
+        self.stream = stream
+        self.h = bs_create(self.cfg, stream)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        self.beam_idx = torch.empty((batch, beam), dtype=torch.int32, device=dev)
+        self.token_id = torch.empty((batch, beam), dtype=torch.int32, device=dev)
+        self.scores = torch.empty((batch, beam), dtype=torch.float32, device=dev)
+        self.done = torch.empty(batch, dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    @classmethod
+    def for_workload(cls, wl, **over):
+        kw = dict(batch=wl.batch, beam=wl.beam, vocab=wl.vocab, max_steps=wl.max_steps,
+                  eos_id=wl.eos_id, pad_id=wl.pad_id, dtype=wl.dtype, lp=wl.lp,
+                  alpha=wl.alpha, stop=wl.stop, num_return=wl.num_return)
+        kw.update(over)
+        return cls(**kw)
+
+    def close(self):
+        if getattr(self, "h", None):
+            bs_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self):
+        bs_reset(self.h)
+
+    @property
+    def steps(self) -> int:
+        return bs_steps_taken(self.h)
+
+    def step(self, logits):
+        bs_step(self.h, logits, self.beam_idx, self.token_id, self.scores, self.done)
+        return self.beam_idx, self.token_id, self.scores, self.done
+
+    def reorder_kv(self, planes_or_desc, gen_len: int, pos_offset: int = 0):
+        d = planes_or_desc
+        if not isinstance(d, bs_kv_desc):
+            d = make_kv_desc(d, pos_offset)
+        bs_reorder_kv(self.h, d, gen_len)
+
+    def selection(self):
+        import torch
+        j = torch.empty((self.B, self.W), dtype=torch.int32, device=self.device)
+        c = torch.empty((self.B, self.W), dtype=torch.float32, device=self.device)
+        bs_last_selection(self.h, j, c)
+        return j, c
+
+    def finished(self):
+        import torch
+        kw = dict(device=self.device)
+        norm = torch.empty((self.B, self.W), dtype=torch.float32, **kw)
+        raw = torch.empty_like(norm)
+        ln = torch.empty((self.B, self.W), dtype=torch.int32, **kw)
+        st, rk = torch.empty_like(ln), torch.empty_like(ln)
+        cnt = torch.empty(self.B, dtype=torch.int32, **kw)
+        bs_get_finished(self.h, norm, raw, ln, st, rk, cnt)
+        return norm, raw, ln, st, rk, cnt
+
+    def finalize(self):
+        import torch
+        R = self.num_return
+        tok = torch.empty((self.B, R, self.T), dtype=torch.int32, device=self.device)
+        ln = torch.empty((self.B, R), dtype=torch.int32, device=self.device)
+        nm = torch.empty((self.B, R), dtype=torch.float32, device=self.device)
+        bs_finalize(self.h, tok, ln, nm)
+        return tok, ln, nm
+
+
+class Verifier:
+    """Blockwise-parallel verify for logits [B, k, V] on the current GPU."""
+
+    def __init__(self, batch, k, vocab, dtype="f32", stream=None):
+        import torch
+        self.B, self.k, self.V = batch, k, vocab
+        self.h = bs_verify_create(batch, k, vocab, DTYPES[dtype], stream)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        self.accept_len = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.argmax = torch.empty((batch, k), dtype=torch.int32, device=dev)
+
+    def close(self):
+        if getattr(self, "h", None):
+            bs_verify_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __call__(self, logits, proposals):
+        bs_verify(self.h, logits, proposals, self.accept_len, self.argmax)
+        return self.accept_len, self.argmax

@@ -1,0 +1,1537 @@
+// beamstep.hip -- HIP kernels and host runtime of libbeamstep.so (gfx950).
+//
+// One decode step of batched beam search ("llm_internals" 9.2.2: expand,
+// score, prune, finalize; the batched section of "Transformers中的Beam
+// Search高效实现") as three kernels per step, plus the verify step of
+// blockwise parallel decoding ("Blockwise Parallel Decoding", section 3):
+//
+//   K1 expand_select   grid (tiles, rows). Streams each live row's logits once
+//                      with 16-byte loads. Per (row, tile) it leaves the
+//                      online softmax partial (max m, sum exp(x - m)) and the
+//                      tile's W best raw logits ordered by (x desc, v asc).
+//                      Log-softmax is monotone within a row, so the union of
+//                      the tile lists holds the row's top-W candidates (the
+//                      same argument as the coarse-to-fine selection in the
+//                      LightSeq article, "层级式解码计算").
+//   K2 merge_finalize  grid (B). Combines the partials into lse per row,
+//                      forms cand = fp32(s + fp32(x - lse)) for the W*tiles*W
+//                      listed candidates, takes the top-W by (cand desc, j
+//                      asc), then runs the finalize sub-step: EOS selections
+//                      into the finished set with the length penalty,
+//                      compaction of live slots in rank order, backpointers,
+//                      the stop rule, and the plan for the KV reorder.
+//   K3 kv_reorder      grid (tiles, B, planes). Each thread reads one 16-byte
+//                      word of every distinct parent row, waits, and writes it
+//                      to every slot that moved, so swaps and cycles are safe
+//                      in place and a shared parent is read once.
+//   K4 verify          grid (tiles, rows) argmax partials, then one wave per
+//                      item for the argmax merge and the accepted prefix.
+//   K5 finalize        grid (B). Final ranking and backtrace of the tokens.
+//
+// No matrix cores: nothing here is a dense contraction. Every kernel is bound
+// by HBM bandwidth.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "beamstep.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int kThreads = 256;           // workgroup size of K1, K2, K3, K4
+constexpr int kWaves = kThreads / 64;   // wave64
+constexpr int kMaxBeam = 16;
+constexpr int kListCap = 1024;          // LDS candidate list of the top-W
+constexpr int kGroups = kThreads / 16;  // 16-lane groups for the selection bound
+constexpr int kMergeNE = 8;             // K2 candidates per thread per batch
+constexpr int kPlanStride = 64;         // int32 words per item of the KV plan
+constexpr int kMaxPlanesPerLaunch = 128;
+constexpr float kInf = __builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+// Selection order: larger key first; equal keys go to the smaller index.
+__device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
+  return xa > xb || (xa == xb && ia < ib);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Combine two (max, sum of exp(x - max)) partials of a log-sum-exp.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  float M = fmaxf(m, m2);
+  if (M == -kInf) {
+    m = -kInf;
+    s = 0.0f;
+    return;
+  }
+  float a = (m == -kInf) ? 0.0f : s * exp2f((m - M) * kLog2e);
+  float c = (m2 == -kInf) ? 0.0f : s2 * exp2f((m2 - M) * kLog2e);
+  m = M;
+  s = a + c;
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions
+// ---------------------------------------------------------------------------
+
+// Butterfly sum over the wave (every lane gets the same, reproducible value).
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// workgroup top-W of register-held (key, index) candidates
+// ---------------------------------------------------------------------------
+
+template <int WMAX>
+struct SelSmem {
+  float gmax[kGroups];
+  float wmax[kWaves];
+  float wsum[kWaves];
+  float rx[kWaves];
+  int ri[kWaves];
+  float tau;
+  int count;
+  float ox[WMAX];
+  int oi[WMAX];
+  alignas(16) float lx[kListCap];
+  alignas(16) int li[kListCap];
+};
+
+// Resets the selection scratch; a barrier must follow before it is used.
+template <int WMAX>
+__device__ __forceinline__ void sel_init(SelSmem<WMAX>& sm) {
+  if (threadIdx.x == 0) {
+    sm.count = 0;
+    sm.tau = -kInf;
+  }
+  if (threadIdx.x < WMAX) {
+    sm.ox[threadIdx.x] = -kInf;
+    sm.oi[threadIdx.x] = 0x7fffffff;
+  }
+}
+
+// Step 1 of the selection. m is this thread's largest key. The workgroup's
+// threads form kGroups groups of 16 lanes; each group's maximum goes to
+// sm.gmax and each wave's maximum to sm.wmax. Returns the wave maximum.
+__device__ __forceinline__ float group_maxima(float m, float* gmax, float* wmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((lane & 15) == 0) gmax[threadIdx.x >> 4] = m;
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (lane == 0) wmax[wave] = m;
+  return m;
+}
+
+// Step 2 (after a barrier): tau = the w_keep-th largest of the group maxima.
+// The group maxima are distinct elements, so at least w_keep elements are
+// >= tau: it is a lower bound on the w_keep-th best key. When fewer than
+// w_keep groups hold a finite key, tau is -inf. Ends with a barrier.
+template <int WMAX>
+__device__ __forceinline__ void group_tau(SelSmem<WMAX>& sm, int w_keep) {
+  const int g = threadIdx.x;
+  if (g < kGroups) {
+    const float v = sm.gmax[g];
+    int rank = 0;
+#pragma unroll
+    for (int h = 0; h < kGroups; ++h) {
+      const float u = sm.gmax[h];
+      rank += (u > v || (u == v && h < g)) ? 1 : 0;
+    }
+    if (rank == w_keep - 1) sm.tau = v;
+  }
+  __syncthreads();
+}
+
+// Step 3: the w_keep (<= WMAX) best of all candidates held by the workgroup,
+// written to sm.ox/sm.oi in rank order; ranks without a finite candidate keep
+// (-inf, INT_MAX). Keys of -inf are never candidates; indices are unique.
+// Only keys >= sm.tau are listed in LDS and ranked by counting. A list that
+// would overflow (massive ties) falls back to w_keep rounds of a workgroup
+// argmax over the registers. Ends with a barrier.
+template <int WMAX, int NE, typename IdFn>
+__device__ void select_from_tau(const float (&x)[NE], IdFn idf, int w_keep, SelSmem<WMAX>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float tau = sm.tau;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) c += (x[i] > -kInf && x[i] >= tau) ? 1 : 0;
+  int p = c ? atomicAdd(&sm.count, c) : 0;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    if (x[i] > -kInf && x[i] >= tau) {
+      if (p < kListCap) {
+        sm.lx[p] = x[i];
+        sm.li[p] = idf(i);
+      }
+      ++p;
+    }
+  }
+  __syncthreads();
+  const int n = sm.count;
+  if (n <= kListCap) {
+    for (int e = tid; e < n; e += kThreads) {
+      const float xe = sm.lx[e];
+      const int ie = sm.li[e];
+      int rank = 0;
+      // four list entries per 16-byte LDS read
+      for (int f0 = 0; f0 < n; f0 += 4) {
+        const float4 xs = *reinterpret_cast<const float4*>(&sm.lx[f0]);
+        const int4 is = *reinterpret_cast<const int4*>(&sm.li[f0]);
+        rank += (f0 + 0 < n && better(xs.x, is.x, xe, ie)) ? 1 : 0;
+        rank += (f0 + 1 < n && better(xs.y, is.y, xe, ie)) ? 1 : 0;
+        rank += (f0 + 2 < n && better(xs.z, is.z, xe, ie)) ? 1 : 0;
+        rank += (f0 + 3 < n && better(xs.w, is.w, xe, ie)) ? 1 : 0;
+      }
+      if (rank < w_keep) {
+        sm.ox[rank] = xe;
+        sm.oi[rank] = ie;
+      }
+    }
+  } else {
+    // Repeated extraction of the best key strictly worse than the previous
+    // one. Uniform control flow: n is the same for every thread.
+    float px = kInf;
+    int pi = -1;
+    for (int r = 0; r < w_keep; ++r) {
+      float bx = -kInf;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int ii = idf(i);
+        if (x[i] > -kInf && better(px, pi, x[i], ii) && better(x[i], ii, bx, bi)) {
+          bx = x[i];
+          bi = ii;
+        }
+      }
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ox = __shfl_xor(bx, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ox, oi, bx, bi)) {
+          bx = ox;
+          bi = oi;
+        }
+      }
+      __syncthreads();
+      if (lane == 0) {
+        sm.rx[wave] = bx;
+        sm.ri[wave] = bi;
+      }
+      __syncthreads();
+      bx = sm.rx[0];
+      bi = sm.ri[0];
+      for (int w = 1; w < kWaves; ++w)
+        if (better(sm.rx[w], sm.ri[w], bx, bi)) {
+          bx = sm.rx[w];
+          bi = sm.ri[w];
+        }
+      if (bx == -kInf) break;
+      if (tid == 0) {
+        sm.ox[r] = bx;
+        sm.oi[r] = bi;
+      }
+      px = bx;
+      pi = bi;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// logits loading: EPT elements per thread, 16-byte vectors when aligned
+// ---------------------------------------------------------------------------
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static float load1(const float* p) { return *p; }
+  __device__ static void loadv(const float* p, float* out) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  }
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static void loadv(const uint16_t* p, float* out) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = __uint_as_float(w[k] << 16);
+      out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+};
+
+// Element i of this thread's tile slice, with its column index:
+//   aligned:   v = v0 + ((i / VEC) * kThreads + tid) * VEC + i % VEC
+//   unaligned: v = v0 + i * kThreads + tid
+template <typename T, bool ALIGNED>
+struct TileMap {
+  static constexpr int kVec = ALIGNED ? Elem<T>::kVec : 1;
+  __device__ static int col(int v0, int i) {
+    return v0 + ((i / kVec) * kThreads + (int)threadIdx.x) * kVec + (i % kVec);
+  }
+};
+
+template <typename T, int EPT, bool ALIGNED>
+__device__ __forceinline__ void load_tile(const T* row, int v0, int vend, float (&x)[EPT]) {
+  constexpr int VEC = TileMap<T, ALIGNED>::kVec;
+#pragma unroll
+  for (int q = 0; q < EPT / VEC; ++q) {
+    const int v = v0 + (q * kThreads + (int)threadIdx.x) * VEC;
+    if (ALIGNED && v + VEC <= vend) {
+      Elem<T>::loadv(row + v, &x[q * VEC]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k)
+        x[q * VEC + k] = (v + k < vend) ? Elem<T>::load1(row + v + k) : -kInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1: expand + local top-W per (row, tile)
+// ---------------------------------------------------------------------------
+
+struct K1Args {
+  const void* logits;
+  int64_t stride;       // elements between rows
+  int V;
+  int W;                // runtime beam width (<= WMAX)
+  int tile;             // elements per tile (kThreads * EPT)
+  int tiles;            // tiles per row
+  const float* s;       // running scores [B*W]
+  const uint8_t* done;  // [B]
+  float* pm;            // [rows][tiles] tile maximum
+  float* ps;            // [rows][tiles] sum of exp(x - tile maximum)
+  float* px;            // [rows][tiles][WMAX] tile top-W logits
+  int* pv;              // [rows][tiles][WMAX] their columns
+};
+
+template <int WMAX, typename T, int EPT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
+  __shared__ SelSmem<WMAX> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int b = r / a.W;
+  const bool skip = a.done[b] != 0;
+  const float sr = a.s[r];
+  if (skip || sr == -kInf) return;  // nothing to expand
+  const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
+  const int v0 = c * a.tile;
+  const int vend = min(a.V, v0 + a.tile);
+
+  float x[EPT];
+  load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
+  sel_init(sm);
+
+  // the tile maximum M, and the 16-lane group maxima that bound the W-th best
+  float tmax = -kInf;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) tmax = fmaxf(tmax, x[i]);
+  group_maxima(tmax, sm.gmax, sm.wmax);
+  __syncthreads();
+  float M = sm.wmax[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wmax[w]);
+
+  // expand: sum of exp(x - M) over the tile
+  float s = 0.0f;
+  if (M > -kInf) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) s += exp2f((x[i] - M) * kLog2e);
+  }
+  s = wave_sum(s);
+  if (lane == 0) sm.wsum[wave] = s;
+
+  // prune, stage 1: the tile's best W raw logits (monotone in log-prob)
+  group_tau(sm, a.W);
+  select_from_tau<WMAX, EPT>(x, [&](int i) { return TileMap<T, ALIGNED>::col(v0, i); }, a.W,
+                             sm);
+
+  const int64_t pt = (int64_t)r * a.tiles + c;
+  if (tid == 0) {
+    float S = sm.wsum[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) S += sm.wsum[w];
+    a.pm[pt] = M;
+    a.ps[pt] = S;
+  }
+  if (tid < WMAX) {
+    a.px[pt * WMAX + tid] = sm.ox[tid];
+    a.pv[pt * WMAX + tid] = sm.oi[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: merge + score + prune + finalize, one workgroup per batch item
+// ---------------------------------------------------------------------------
+
+struct DevState {
+  float* s;            // [B*W] running scores, -inf = dead slot
+  int* slot_rank;      // [B*W] rank of the slot's last selection
+  uint8_t* done;       // [B]
+  float* hnorm;        // [B*W] finished set
+  float* hraw;
+  int* hlen;
+  int* hstep;
+  int* hrank;
+  int* hpar;           // parent slot at step-1
+  int* htok;           // last token
+  int* hcount;         // [B]
+  int* bp_par;         // [T][B][W]
+  int* bp_tok;         // [T][B][W]
+  int* sel_j;          // [B][W]
+  float* sel_c;        // [B][W]
+  int* plan;           // [B][kPlanStride]
+  const double* lpt;   // [T+1] length penalty per length
+};
+
+struct K2Args {
+  DevState st;
+  const float* pm;
+  const float* ps;
+  const float* px;
+  const int* pv;
+  int B, W, V, T, tiles, eos, pad, stop;
+  double alpha;
+  int t;               // this step, 1-based
+  int32_t* out_beam;
+  int32_t* out_tok;
+  float* out_score;
+  uint8_t* out_done;
+};
+
+__device__ __forceinline__ bool hyp_better(float na, int sa, int ra, float nb, int sb, int rb) {
+  if (na != nb) return na > nb;
+  if (sa != sb) return sa < sb;
+  return ra < rb;
+}
+
+// The finished set of one item, staged in LDS for the finalize.
+template <int WMAX>
+struct HypSmem {
+  float norm[WMAX], raw[WMAX];
+  int len[WMAX], step[WMAX], rank[WMAX], par[WMAX], tok[WMAX];
+  int count;
+};
+
+// BeamHypotheses.add of the batched section: append while fewer than W are
+// kept, else replace the worst kept hypothesis when strictly better.
+template <int WMAX>
+__device__ void hyp_insert(HypSmem<WMAX>& h, int W, float norm, float raw, int len, int step,
+                           int rank, int par, int tok) {
+  int slot;
+  if (h.count < W) {
+    slot = h.count++;
+  } else {
+    int worst = 0;
+    for (int i = 1; i < W; ++i)
+      if (hyp_better(h.norm[worst], h.step[worst], h.rank[worst], h.norm[i], h.step[i],
+                     h.rank[i]))
+        worst = i;
+    if (!hyp_better(norm, step, rank, h.norm[worst], h.step[worst], h.rank[worst])) return;
+    slot = worst;
+  }
+  h.norm[slot] = norm;
+  h.raw[slot] = raw;
+  h.len[slot] = len;
+  h.step[slot] = step;
+  h.rank[slot] = rank;
+  h.par[slot] = par;
+  h.tok[slot] = tok;
+}
+
+template <int WMAX>
+__global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
+  constexpr int kStage = 4 * kThreads;  // tile partials staged per pass
+  __shared__ SelSmem<WMAX> sm;
+  __shared__ HypSmem<WMAX> hy;
+  __shared__ float lse[WMAX];
+  __shared__ float srow[WMAX];
+  __shared__ float stage_m[kStage], stage_s[kStage];
+  __shared__ float lse_m[WMAX], lse_s[WMAX];
+  __shared__ int nslot_par[WMAX], nslot_tok[WMAX], nslot_rank[WMAX];
+  __shared__ float nslot_s[WMAX];
+  __shared__ int plan[kPlanStride];
+  __shared__ int live_sh, done_sh;
+  __shared__ double lp_t, lp_T;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = a.W, V = a.V, t = a.t;
+  const DevState& st = a.st;
+  const int bpbase = ((t - 1) * a.B + b) * W;
+  const int n_part = W * a.tiles;
+  const int per_row = a.tiles * WMAX;
+  const int n_entries = W * per_row;
+  const float* px = a.px + (int64_t)b * n_entries;
+  const int* pv = a.pv + (int64_t)b * n_entries;
+
+  // every load of the item's state and of the first batch is issued up front
+  float lx[kMergeNE];
+  int lv[kMergeNE];
+#pragma unroll
+  for (int q = 0; q < kMergeNE; ++q) {
+    const int e = q * kThreads + tid;
+    lx[q] = e < n_entries ? px[e] : -kInf;
+    lv[q] = e < n_entries ? pv[e] : 0;
+  }
+  for (int k = 0; k < kStage / kThreads; ++k) {
+    const int e = k * kThreads + tid;
+    if (e < n_part) {
+      stage_m[e] = a.pm[(int64_t)b * n_part + e];
+      stage_s[e] = a.ps[(int64_t)b * n_part + e];
+    }
+  }
+  if (tid < W) {
+    const int e = b * W + tid;
+    srow[tid] = st.s[e];
+    hy.norm[tid] = st.hnorm[e];
+    hy.raw[tid] = st.hraw[e];
+    hy.len[tid] = st.hlen[e];
+    hy.step[tid] = st.hstep[e];
+    hy.rank[tid] = st.hrank[e];
+    hy.par[tid] = st.hpar[e];
+    hy.tok[tid] = st.htok[e];
+    lse_m[tid] = -kInf;
+    lse_s[tid] = 0.0f;
+  }
+  if (tid == 0) {
+    done_sh = st.done[b];
+    hy.count = st.hcount[b];
+    lp_t = st.lpt[t];
+    lp_T = st.lpt[a.T];
+  }
+  sel_init(sm);
+  __syncthreads();
+
+  if (done_sh) {  // finished items: no-op outputs
+    if (tid < W) {
+      a.out_beam[b * W + tid] = tid;
+      a.out_tok[b * W + tid] = a.pad;
+      a.out_score[b * W + tid] = -kInf;
+      st.bp_par[bpbase + tid] = tid;
+      st.bp_tok[bpbase + tid] = a.pad;
+      st.sel_j[b * W + tid] = -1;
+      st.sel_c[b * W + tid] = -kInf;
+    }
+    if (tid == 0) {
+      a.out_done[b] = 1;
+      st.plan[b * kPlanStride + 1] = 0;
+    }
+    return;
+  }
+
+  // expand: lse of every live row from its tile partials. One wave per row,
+  // lanes over tiles: the row maximum, then sum of S_tile * exp(M_tile - M),
+  // both with fixed reduction trees.
+  for (int base = 0; base < n_part; base += kStage) {
+    if (base > 0) {
+      __syncthreads();
+      for (int k = 0; k < kStage / kThreads; ++k) {
+        const int e = base + k * kThreads + tid;
+        if (e < n_part) {
+          stage_m[e - base] = a.pm[(int64_t)b * n_part + e];
+          stage_s[e - base] = a.ps[(int64_t)b * n_part + e];
+        }
+      }
+      __syncthreads();
+    }
+    for (int w = wave; w < W; w += kWaves) {
+      if (!(srow[w] > -kInf)) continue;
+      const int lo = max(base, w * a.tiles), hi = min(base + kStage, (w + 1) * a.tiles);
+      float m = -kInf;
+      for (int e = lo + lane; e < hi; e += 64) m = fmaxf(m, stage_m[e - base]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      float sum = 0.0f;
+      if (m > -kInf)
+        for (int e = lo + lane; e < hi; e += 64) {
+          const float mt = stage_m[e - base];
+          if (mt > -kInf) sum += stage_s[e - base] * exp2f((mt - m) * kLog2e);
+        }
+      sum = wave_sum(sum);
+      if (lane == 0) {  // combine with the previous pass (tiles beyond kStage)
+        float pm = lse_m[w], ps = lse_s[w];
+        lse_combine(pm, ps, m, sum);
+        lse_m[w] = pm;
+        lse_s[w] = ps;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < W) lse[tid] = (srow[tid] > -kInf && lse_m[tid] > -kInf) ? lse_m[tid] + logf(lse_s[tid])
+                                                                   : -kInf;
+  __syncthreads();
+
+  // score + prune: top-W over the listed candidates, in batches, carrying the
+  // running top-W from one batch to the next
+  float carry_x = -kInf;
+  int carry_i = 0x7fffffff;
+  for (int base = 0; base < n_entries; base += kThreads * kMergeNE) {
+    if (base > 0) {
+#pragma unroll
+      for (int q = 0; q < kMergeNE; ++q) {
+        const int e = base + q * kThreads + tid;
+        lx[q] = e < n_entries ? px[e] : -kInf;
+        lv[q] = e < n_entries ? pv[e] : 0;
+      }
+    }
+    float x[kMergeNE + 1];
+    int id[kMergeNE + 1];
+    float gm = carry_x;
+#pragma unroll
+    for (int q = 0; q < kMergeNE; ++q) {
+      const int e = base + q * kThreads + tid;
+      const int w = e / per_row;
+      x[q] = -kInf;
+      id[q] = 0x7fffffff;
+      if (e < n_entries) {
+        const float lw = lse[w];
+        if (lx[q] > -kInf && lw > -kInf) {
+          const float logp = lx[q] - lw;   // fp32 log-probability
+          x[q] = srow[w] + logp;           // fp32 candidate score
+          id[q] = w * V + lv[q];
+        }
+      }
+      gm = fmaxf(gm, x[q]);
+    }
+    x[kMergeNE] = carry_x;
+    id[kMergeNE] = carry_i;
+    __syncthreads();  // the carry was read from sm.ox before sm is reused
+    sel_init(sm);
+    group_maxima(gm, sm.gmax, sm.wmax);
+    __syncthreads();
+    group_tau(sm, W);
+    select_from_tau<WMAX, kMergeNE + 1>(x, [&](int i) { return id[i]; }, W, sm);
+    if (tid < W) {
+      carry_x = sm.ox[tid];
+      carry_i = sm.oi[tid];
+    } else {
+      carry_x = -kInf;
+      carry_i = 0x7fffffff;
+    }
+  }
+
+  // finalize (one thread, on LDS; W <= 16 selections)
+  if (tid == 0) {
+    int live = 0;
+    float best_raw = -kInf;
+    for (int k = 0; k < W; ++k) {
+      const float c = sm.ox[k];
+      const int j = sm.oi[k];
+      if (!(c > -kInf)) continue;
+      if (best_raw == -kInf) best_raw = c;
+      const int p = j / V;
+      const int tok = j - p * V;
+      if (a.eos >= 0 && tok == a.eos) {
+        const float norm = (float)((double)c / lp_t);
+        hyp_insert(hy, W, norm, c, t, t, k, p, tok);
+      } else {
+        nslot_par[live] = p;
+        nslot_tok[live] = tok;
+        nslot_rank[live] = k;
+        nslot_s[live] = c;
+        ++live;
+      }
+    }
+    int d = 0;
+    if (live == 0) {
+      d = 1;
+    } else if (hy.count == W) {
+      float worst = kInf;
+      for (int i = 0; i < W; ++i) worst = fminf(worst, hy.norm[i]);
+      if (a.stop == BS_STOP_TRUE) {
+        d = 1;
+      } else if (a.stop == BS_STOP_HEURISTIC) {
+        d = worst >= (float)((double)best_raw / lp_t);
+      } else {
+        const float best_live = nslot_s[0];
+        const double lp = (a.alpha > 0.0 && best_live <= 0.0f) ? lp_T : lp_t;
+        d = worst >= (float)((double)best_live / lp);
+      }
+    }
+    live_sh = live;
+    st.done[b] = (uint8_t)d;
+    a.out_done[b] = (uint8_t)d;
+
+    // reorder plan: distinct parents of the slots that moved, each with the
+    // list of slots it is copied to (grouped by parent)
+    int nsrc = 0, ndst = 0;
+    if (!d) {
+      for (int i = 0; i < live; ++i) {
+        const int p = nslot_par[i];
+        if (p == i) continue;
+        bool seen = false;
+        for (int q = 0; q < nsrc; ++q) seen |= (plan[2 + q] == p);
+        if (!seen) plan[2 + nsrc++] = p;
+      }
+      for (int q = 0; q < nsrc; ++q) {
+        int cnt = 0;
+        for (int i = 0; i < live; ++i) {
+          if (nslot_par[i] != i && nslot_par[i] == plan[2 + q]) {
+            plan[2 + 2 * kMaxBeam + ndst++] = i;
+            ++cnt;
+          }
+        }
+        plan[2 + kMaxBeam + q] = cnt;
+      }
+    }
+    plan[0] = nsrc;
+    plan[1] = ndst;
+  }
+  __syncthreads();
+
+  // write back: plan, finished set, selection, compacted slots (live ones in
+  // rank order, then dead ones), backpointers
+  if (tid < 2 + 3 * kMaxBeam) st.plan[b * kPlanStride + tid] = plan[tid];
+  if (tid < W) {
+    const int e = b * W + tid;
+    st.hnorm[e] = hy.norm[tid];
+    st.hraw[e] = hy.raw[tid];
+    st.hlen[e] = hy.len[tid];
+    st.hstep[e] = hy.step[tid];
+    st.hrank[e] = hy.rank[tid];
+    st.hpar[e] = hy.par[tid];
+    st.htok[e] = hy.tok[tid];
+    const float c = sm.ox[tid];
+    st.sel_j[e] = (c > -kInf) ? sm.oi[tid] : -1;
+    st.sel_c[e] = c;
+    const int i = tid;
+    if (i < live_sh) {
+      st.s[e] = nslot_s[i];
+      st.slot_rank[e] = nslot_rank[i];
+      a.out_beam[e] = nslot_par[i];
+      a.out_tok[e] = nslot_tok[i];
+      a.out_score[e] = nslot_s[i];
+      st.bp_par[bpbase + i] = nslot_par[i];
+      st.bp_tok[bpbase + i] = nslot_tok[i];
+    } else {
+      st.s[e] = -kInf;
+      st.slot_rank[e] = W;
+      a.out_beam[e] = i;
+      a.out_tok[e] = a.pad;
+      a.out_score[e] = -kInf;
+      st.bp_par[bpbase + i] = i;
+      st.bp_tok[bpbase + i] = a.pad;
+    }
+  }
+  if (tid == 0) st.hcount[b] = hy.count;
+}
+
+// ---------------------------------------------------------------------------
+// K3: in-place KV reorder
+// ---------------------------------------------------------------------------
+
+struct K3Args {
+  char* planes[kMaxPlanesPerLaunch];
+  int64_t row_stride;   // bytes
+  int64_t pos_stride;   // bytes
+  int64_t base_off;     // pos_offset * pos_stride, bytes
+  int64_t words;        // words per row to move: gen_len * words_per_pos
+  int64_t words_per_pos;
+  int W;
+  const int* plan;
+};
+
+template <int WORD>
+struct Word;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <>
+struct Word<16> {
+  using type = u32x4;
+};
+template <>
+struct Word<4> {
+  using type = uint32_t;
+};
+
+template <int WMAX, int WORD, int NP, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k3_kv_reorder(K3Args a) {
+  using WT = typename Word<WORD>::type;
+  const int b = blockIdx.y;
+  const int* plan = a.plan + b * kPlanStride;
+  const int ndst = plan[1];
+  if (ndst == 0) return;
+  const int nsrc = plan[0];
+  char* base = a.planes[blockIdx.z] + a.base_off;
+  const int64_t row0 = (int64_t)b * a.W;
+
+  int64_t off[NP];
+  bool ok[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int64_t e = ((int64_t)blockIdx.x * NP + k) * kThreads + threadIdx.x;
+    ok[k] = e < a.words;
+    if (CONTIG) {
+      off[k] = e * WORD;
+    } else {
+      const int64_t pos = e / a.words_per_pos;
+      off[k] = pos * a.pos_stride + (e - pos * a.words_per_pos) * WORD;
+    }
+  }
+
+  WT v[NP][WMAX];
+#pragma unroll
+  for (int q = 0; q < WMAX; ++q) {
+    if (q < nsrc) {
+      const char* src = base + (row0 + plan[2 + q]) * a.row_stride;
+#pragma unroll
+      for (int k = 0; k < NP; ++k)
+        if (ok[k]) v[k][q] = *reinterpret_cast<const WT*>(src + off[k]);
+    }
+  }
+  // every parent word this thread moves has been read before any is written
+  __syncthreads();
+  int d = 0;
+#pragma unroll
+  for (int q = 0; q < WMAX; ++q) {
+    if (q < nsrc) {
+      const int cnt = plan[2 + kMaxBeam + q];
+      for (int u = 0; u < cnt; ++u, ++d) {
+        char* dst = base + (row0 + plan[2 + 2 * kMaxBeam + d]) * a.row_stride;
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+          if (ok[k]) *reinterpret_cast<WT*>(dst + off[k]) = v[k][q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4: blockwise verify
+// ---------------------------------------------------------------------------
+
+struct K4Args {
+  const void* logits;
+  int64_t stride;
+  int V, tile, tiles, k, B;
+  float* px;   // [rows][tiles]
+  int* pv;     // [rows][tiles]
+  const int32_t* proposals;
+  int32_t* accept;
+  int32_t* argmax;
+};
+
+template <typename T, int EPT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void k4_argmax_tiles(K4Args a) {
+  __shared__ float rx[kWaves];
+  __shared__ int ri[kWaves];
+  const int r = blockIdx.y, c = blockIdx.x;
+  const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
+  const int v0 = c * a.tile;
+  const int vend = min(a.V, v0 + a.tile);
+  float x[EPT];
+  load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
+  // first index of the maximum; -inf logits take part (padding is excluded)
+  float bx = -kInf;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int v = TileMap<T, ALIGNED>::col(v0, i);
+    if (v < vend && better(x[i], v, bx, bi)) {
+      bx = x[i];
+      bi = v;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float ox = __shfl_xor(bx, o);
+    int oi = __shfl_xor(bi, o);
+    if (better(ox, oi, bx, bi)) {
+      bx = ox;
+      bi = oi;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    rx[wave] = bx;
+    ri[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      if (better(rx[w], ri[w], bx, bi)) {
+        bx = rx[w];
+        bi = ri[w];
+      }
+    a.px[(int64_t)r * a.tiles + c] = bx;
+    a.pv[(int64_t)r * a.tiles + c] = bi;
+  }
+}
+
+// one wave per item: lane i merges the tiles of position i
+__global__ __launch_bounds__(64) void k4_accept(K4Args a) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  bool match = false;
+  if (i < a.k) {
+    const int64_t r = (int64_t)b * a.k + i;
+    float bx = -kInf;
+    int bi = 0x7fffffff;
+    for (int c = 0; c < a.tiles; ++c) {
+      const float x = a.px[r * a.tiles + c];
+      const int v = a.pv[r * a.tiles + c];
+      if (better(x, v, bx, bi)) {
+        bx = x;
+        bi = v;
+      }
+    }
+    a.argmax[r] = bi;
+    match = (a.proposals[r] == bi);
+  }
+  const uint64_t m = __ballot(match);
+  if (i == 0) {
+    // accepted prefix: number of trailing ones of the match mask, at most k
+    const uint64_t miss = ~m;
+    int acc = (miss == 0) ? 64 : __ffsll((long long)miss) - 1;
+    a.accept[b] = acc < a.k ? acc : a.k;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K5: final selection and backtrace
+// ---------------------------------------------------------------------------
+
+struct K5Args {
+  DevState st;
+  int B, W, T, pad, R, steps;
+  int32_t* tokens;     // [B][R][T]
+  int32_t* lengths;    // [B][R]
+  float* norms;        // [B][R]
+};
+
+template <int WMAX>
+__global__ __launch_bounds__(64) void k5_finalize(K5Args a) {
+  __shared__ float hn[2 * WMAX];
+  __shared__ int hs[2 * WMAX], hr[2 * WMAX], hl[2 * WMAX], hp[2 * WMAX], ht[2 * WMAX];
+  __shared__ int order[2 * WMAX];
+  __shared__ int nh;
+  const int b = blockIdx.x, tid = threadIdx.x, W = a.W;
+  const DevState& st = a.st;
+  if (tid == 0) {
+    // a copy of the finished set, then the live beams of an unfinished item
+    int n = st.hcount[b];
+    for (int i = 0; i < n; ++i) {
+      hn[i] = st.hnorm[b * W + i];
+      hs[i] = st.hstep[b * W + i];
+      hr[i] = st.hrank[b * W + i];
+      hl[i] = st.hlen[b * W + i];
+      hp[i] = st.hpar[b * W + i];
+      ht[i] = st.htok[b * W + i];
+    }
+    if (!st.done[b]) {
+      const int T1 = a.steps;
+      const int bp = ((T1 - 1) * a.B + b) * W;
+      for (int i = 0; i < W; ++i) {
+        const float s = st.s[b * W + i];
+        if (!(s > -kInf)) continue;
+        const float norm = (float)((double)s / st.lpt[T1]);
+        const int rank = st.slot_rank[b * W + i];
+        int slot;
+        if (n < W) {
+          slot = n++;
+        } else {
+          int worst = 0;
+          for (int q = 1; q < W; ++q)
+            if (hyp_better(hn[worst], hs[worst], hr[worst], hn[q], hs[q], hr[q])) worst = q;
+          if (!hyp_better(norm, T1, rank, hn[worst], hs[worst], hr[worst])) continue;
+          slot = worst;
+        }
+        hn[slot] = norm;
+        hs[slot] = T1;
+        hr[slot] = rank;
+        hl[slot] = T1;
+        hp[slot] = st.bp_par[bp + i];
+        ht[slot] = st.bp_tok[bp + i];
+      }
+    }
+    // best first
+    for (int i = 0; i < n; ++i) order[i] = i;
+    for (int i = 1; i < n; ++i) {
+      int x = order[i], k = i;
+      while (k > 0 && hyp_better(hn[x], hs[x], hr[x], hn[order[k - 1]], hs[order[k - 1]],
+                                 hr[order[k - 1]])) {
+        order[k] = order[k - 1];
+        --k;
+      }
+      order[k] = x;
+    }
+    nh = n;
+  }
+  __syncthreads();
+  for (int r = tid; r < a.R; r += blockDim.x) {
+    int32_t* out = a.tokens + ((int64_t)b * a.R + r) * a.T;
+    for (int i = 0; i < a.T; ++i) out[i] = a.pad;
+    if (r < nh) {
+      const int h = order[r];
+      const int len = hl[h];
+      out[len - 1] = ht[h];
+      int slot = hp[h];
+      for (int u = hs[h] - 1; u >= 1; --u) {
+        const int bp = ((u - 1) * a.B + b) * W + slot;
+        out[u - 1] = st.bp_tok[bp];
+        slot = st.bp_par[bp];
+      }
+      a.lengths[b * a.R + r] = len;
+      a.norms[b * a.R + r] = hn[h];
+    } else {
+      a.lengths[b * a.R + r] = 0;
+      a.norms[b * a.R + r] = -kInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// init: running scores, finished sets, done flags, length-penalty table
+// ---------------------------------------------------------------------------
+
+struct InitArgs {
+  DevState st;
+  double* lpt;
+  int B, W, T, lp;
+  double alpha;
+};
+
+__global__ void k0_init(InitArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.B * a.W) {
+    a.st.s[i] = (i % a.W == 0) ? 0.0f : -kInf;
+    a.st.slot_rank[i] = 0;
+  }
+  if (i < a.B) {
+    a.st.done[i] = 0;
+    a.st.hcount[i] = 0;
+    a.st.plan[i * kPlanStride + 1] = 0;
+  }
+  if (i <= a.T) {
+    double v = 1.0;
+    if (a.lp == BS_LP_GNMT) v = pow((5.0 + (double)i) / 6.0, a.alpha);
+    else if (a.lp == BS_LP_POW) v = pow((double)i, a.alpha);
+    a.lpt[i] = v;
+  }
+}
+
+}  // namespace
+
+// ===========================================================================
+// host runtime
+// ===========================================================================
+
+struct bs_state {
+  bs_config cfg;
+  hipStream_t stream;
+  int device;
+  int B, W, V, T, rows, wmax, ept, tile, tiles;
+  int t;                // steps taken
+  void* block;          // the one device allocation
+  DevState st;
+  double* lpt;
+  float* pm;
+  float* ps;
+  float* px;
+  int* pv;
+};
+
+struct bs_verify_state {
+  hipStream_t stream;
+  int device;
+  int B, k, V, dtype, ept, tile, tiles;
+  void* block;
+  float* px;
+  int* pv;
+};
+
+namespace {
+
+int pow2ceil(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+size_t align_up(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int choose_ept(int rows, int V, int hint) {
+  if (hint == 16 || hint == 32 || hint == 64) return hint;
+  // the largest per-thread tile that still gives >= 1024 workgroups
+  for (int e : {64, 32}) {
+    const int64_t tiles = (V + (int64_t)kThreads * e - 1) / ((int64_t)kThreads * e);
+    if ((int64_t)rows * tiles >= 1024) return e;
+  }
+  return 16;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? BS_OK : BS_EDEVICE; }
+
+// ---- K1 dispatch ----------------------------------------------------------
+template <int WMAX, typename T, int EPT>
+void launch_k1_a(const K1Args& a, bool aligned, dim3 grid, hipStream_t s) {
+  if (aligned)
+    hipLaunchKernelGGL((k1_expand_select<WMAX, T, EPT, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_expand_select<WMAX, T, EPT, false>), grid, dim3(kThreads), 0, s, a);
+}
+template <int WMAX, typename T>
+void launch_k1_e(const K1Args& a, int ept, bool aligned, dim3 grid, hipStream_t s) {
+  if (ept == 64) launch_k1_a<WMAX, T, 64>(a, aligned, grid, s);
+  else if (ept == 32) launch_k1_a<WMAX, T, 32>(a, aligned, grid, s);
+  else launch_k1_a<WMAX, T, 16>(a, aligned, grid, s);
+}
+template <int WMAX>
+void launch_k1_t(const K1Args& a, int dtype, int ept, bool aligned, dim3 grid, hipStream_t s) {
+  if (dtype == BS_BF16) launch_k1_e<WMAX, uint16_t>(a, ept, aligned, grid, s);
+  else launch_k1_e<WMAX, float>(a, ept, aligned, grid, s);
+}
+void launch_k1(const K1Args& a, int wmax, int dtype, int ept, bool aligned, dim3 grid,
+               hipStream_t s) {
+  switch (wmax) {
+    case 1: launch_k1_t<1>(a, dtype, ept, aligned, grid, s); break;
+    case 2: launch_k1_t<2>(a, dtype, ept, aligned, grid, s); break;
+    case 4: launch_k1_t<4>(a, dtype, ept, aligned, grid, s); break;
+    case 8: launch_k1_t<8>(a, dtype, ept, aligned, grid, s); break;
+    default: launch_k1_t<16>(a, dtype, ept, aligned, grid, s); break;
+  }
+}
+
+void launch_k2(const K2Args& a, int wmax, hipStream_t s) {
+  dim3 g(a.B), blk(kThreads);
+  switch (wmax) {
+    case 1: hipLaunchKernelGGL((k2_merge_finalize<1>), g, blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k2_merge_finalize<2>), g, blk, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k2_merge_finalize<4>), g, blk, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k2_merge_finalize<8>), g, blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((k2_merge_finalize<16>), g, blk, 0, s, a); break;
+  }
+}
+
+// ---- K3 dispatch ----------------------------------------------------------
+template <int WMAX, int WORD, bool CONTIG>
+void launch_k3_c(const K3Args& a, int64_t tiles_per_row, int B, int nplanes, hipStream_t s) {
+  constexpr int NP = (16 / WMAX) > 0 ? (16 / WMAX > 4 ? 4 : 16 / WMAX) : 1;
+  const int64_t tiles = (a.words + (int64_t)kThreads * NP - 1) / ((int64_t)kThreads * NP);
+  (void)tiles_per_row;
+  dim3 g((unsigned)tiles, B, nplanes);
+  hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kThreads), 0, s, a);
+}
+template <int WMAX>
+void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s) {
+  if (word == 16) {
+    if (contig) launch_k3_c<WMAX, 16, true>(a, 0, B, nplanes, s);
+    else launch_k3_c<WMAX, 16, false>(a, 0, B, nplanes, s);
+  } else {
+    if (contig) launch_k3_c<WMAX, 4, true>(a, 0, B, nplanes, s);
+    else launch_k3_c<WMAX, 4, false>(a, 0, B, nplanes, s);
+  }
+}
+void launch_k3(const K3Args& a, int wmax, int word, bool contig, int B, int nplanes,
+               hipStream_t s) {
+  switch (wmax) {
+    case 1: launch_k3_w<1>(a, word, contig, B, nplanes, s); break;
+    case 2: launch_k3_w<2>(a, word, contig, B, nplanes, s); break;
+    case 4: launch_k3_w<4>(a, word, contig, B, nplanes, s); break;
+    case 8: launch_k3_w<8>(a, word, contig, B, nplanes, s); break;
+    default: launch_k3_w<16>(a, word, contig, B, nplanes, s); break;
+  }
+}
+
+void launch_k5(const K5Args& a, int wmax, hipStream_t s) {
+  dim3 g(a.B), blk(64);
+  switch (wmax) {
+    case 1: hipLaunchKernelGGL((k5_finalize<1>), g, blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k5_finalize<2>), g, blk, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k5_finalize<4>), g, blk, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k5_finalize<8>), g, blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((k5_finalize<16>), g, blk, 0, s, a); break;
+  }
+}
+
+// ---- K4 dispatch ----------------------------------------------------------
+template <typename T, int EPT>
+void launch_k4_a(const K4Args& a, bool aligned, dim3 grid, hipStream_t s) {
+  if (aligned)
+    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, false>), grid, dim3(kThreads), 0, s, a);
+}
+template <typename T>
+void launch_k4_e(const K4Args& a, int ept, bool aligned, dim3 grid, hipStream_t s) {
+  if (ept == 64) launch_k4_a<T, 64>(a, aligned, grid, s);
+  else if (ept == 32) launch_k4_a<T, 32>(a, aligned, grid, s);
+  else launch_k4_a<T, 16>(a, aligned, grid, s);
+}
+
+int launch_init(bs_state* h) {
+  InitArgs ia;
+  ia.st = h->st;
+  ia.lpt = h->lpt;
+  ia.B = h->B;
+  ia.W = h->W;
+  ia.T = h->T;
+  ia.lp = h->cfg.lp;
+  ia.alpha = h->cfg.alpha;
+  int n = h->B * h->W;
+  if (h->T + 1 > n) n = h->T + 1;
+  hipLaunchKernelGGL(k0_init, dim3((n + 255) / 256), dim3(256), 0, h->stream, ia);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bs_strerror(int status) {
+  switch (status) {
+    case BS_OK: return "ok";
+    case BS_EINVAL: return "invalid argument";
+    case BS_ENOMEM: return "device allocation failed";
+    case BS_EDEVICE: return "HIP runtime error";
+    case BS_ESTATE: return "call not valid in the current state";
+    default: return "unknown status";
+  }
+}
+
+int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
+  if (!cfg || !out) return BS_EINVAL;
+  *out = nullptr;
+  const bs_config c = *cfg;
+  if (c.batch < 1 || c.beam < 1 || c.beam > kMaxBeam || c.vocab < 1 || c.max_steps < 1)
+    return BS_EINVAL;
+  if ((int64_t)c.beam * c.vocab >= ((int64_t)1 << 31)) return BS_EINVAL;
+  if ((int64_t)c.batch * c.beam * c.max_steps >= ((int64_t)1 << 31)) return BS_EINVAL;
+  if (c.logits_dtype != BS_F32 && c.logits_dtype != BS_BF16) return BS_EINVAL;
+  if (c.lp < BS_LP_NONE || c.lp > BS_LP_POW) return BS_EINVAL;
+  if (c.stop < BS_STOP_TRUE || c.stop > BS_STOP_NEVER) return BS_EINVAL;
+  if (c.num_return < 1 || c.num_return > c.beam) return BS_EINVAL;
+  if (c.tile_elems != 0 && c.tile_elems != 16 && c.tile_elems != 32 && c.tile_elems != 64)
+    return BS_EINVAL;
+  if (!(c.alpha == c.alpha)) return BS_EINVAL;
+
+  bs_state* h = (bs_state*)calloc(1, sizeof(bs_state));
+  if (!h) return BS_ENOMEM;
+  h->cfg = c;
+  h->stream = (hipStream_t)hip_stream;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    free(h);
+    return BS_EDEVICE;
+  }
+  h->B = c.batch;
+  h->W = c.beam;
+  h->V = c.vocab;
+  h->T = c.max_steps;
+  h->rows = c.batch * c.beam;
+  h->wmax = pow2ceil(c.beam);
+  h->ept = choose_ept(h->rows, c.vocab, c.tile_elems);
+  h->tile = kThreads * h->ept;
+  h->tiles = (c.vocab + h->tile - 1) / h->tile;
+
+  const size_t RW = (size_t)h->rows;
+  const size_t PT = RW * h->tiles;
+  const size_t BT = (size_t)h->T * RW;
+  size_t sizes[] = {
+      RW * 4,                 // s
+      RW * 4,                 // slot_rank
+      (size_t)h->B,           // done
+      RW * 4, RW * 4, RW * 4, RW * 4, RW * 4, RW * 4, RW * 4,  // finished set
+      (size_t)h->B * 4,       // hcount
+      BT * 4, BT * 4,         // backpointers
+      RW * 4, RW * 4,         // selection
+      (size_t)h->B * kPlanStride * 4,  // plan
+      ((size_t)h->T + 1) * 8, // lpt
+      PT * 4, PT * 4,         // pm, ps
+      PT * h->wmax * 4, PT * h->wmax * 4,  // px, pv
+  };
+  const int n = sizeof(sizes) / sizeof(sizes[0]);
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += align_up(sizes[i]);
+  if (hipMalloc(&h->block, total) != hipSuccess) {
+    (void)hipGetLastError();
+    free(h);
+    return BS_ENOMEM;
+  }
+  char* p = (char*)h->block;
+  void* ptr[n];
+  for (int i = 0; i < n; ++i) {
+    ptr[i] = p;
+    p += align_up(sizes[i]);
+  }
+  int i = 0;
+  h->st.s = (float*)ptr[i++];
+  h->st.slot_rank = (int*)ptr[i++];
+  h->st.done = (uint8_t*)ptr[i++];
+  h->st.hnorm = (float*)ptr[i++];
+  h->st.hraw = (float*)ptr[i++];
+  h->st.hlen = (int*)ptr[i++];
+  h->st.hstep = (int*)ptr[i++];
+  h->st.hrank = (int*)ptr[i++];
+  h->st.hpar = (int*)ptr[i++];
+  h->st.htok = (int*)ptr[i++];
+  h->st.hcount = (int*)ptr[i++];
+  h->st.bp_par = (int*)ptr[i++];
+  h->st.bp_tok = (int*)ptr[i++];
+  h->st.sel_j = (int*)ptr[i++];
+  h->st.sel_c = (float*)ptr[i++];
+  h->st.plan = (int*)ptr[i++];
+  h->lpt = (double*)ptr[i++];
+  h->st.lpt = h->lpt;
+  h->pm = (float*)ptr[i++];
+  h->ps = (float*)ptr[i++];
+  h->px = (float*)ptr[i++];
+  h->pv = (int*)ptr[i++];
+
+  int rc = launch_init(h);
+  if (rc == BS_OK && hipStreamSynchronize(h->stream) != hipSuccess) rc = BS_EDEVICE;
+  if (rc != BS_OK) {
+    (void)hipFree(h->block);
+    free(h);
+    return rc;
+  }
+  *out = h;
+  return BS_OK;
+}
+
+int bs_reset(bs_state* h) {
+  if (!h) return BS_EINVAL;
+  int rc = launch_init(h);
+  if (rc == BS_OK) h->t = 0;
+  return rc;
+}
+
+int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* beam_idx,
+            int32_t* token_id, float* scores, uint8_t* done) {
+  if (!h || !logits || !beam_idx || !token_id || !scores || !done) return BS_EINVAL;
+  if (row_stride_elems < h->V) return BS_EINVAL;
+  if (h->t >= h->T) return BS_ESTATE;
+  const int t = h->t + 1;
+  const int esize = h->cfg.logits_dtype == BS_BF16 ? 2 : 4;
+  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((row_stride_elems * esize) % 16 == 0);
+
+  K1Args a1;
+  a1.logits = logits;
+  a1.stride = row_stride_elems;
+  a1.V = h->V;
+  a1.W = h->W;
+  a1.tile = h->tile;
+  a1.tiles = h->tiles;
+  a1.s = h->st.s;
+  a1.done = h->st.done;
+  a1.pm = h->pm;
+  a1.ps = h->ps;
+  a1.px = h->px;
+  a1.pv = h->pv;
+  launch_k1(a1, h->wmax, h->cfg.logits_dtype, h->ept, aligned, dim3(h->tiles, h->rows),
+            h->stream);
+  int rc = launch_status();
+  if (rc != BS_OK) return rc;
+
+  K2Args a2;
+  a2.st = h->st;
+  a2.pm = h->pm;
+  a2.ps = h->ps;
+  a2.px = h->px;
+  a2.pv = h->pv;
+  a2.B = h->B;
+  a2.W = h->W;
+  a2.V = h->V;
+  a2.T = h->T;
+  a2.tiles = h->tiles;
+  a2.eos = h->cfg.eos_id;
+  a2.pad = h->cfg.pad_id;
+  a2.stop = h->cfg.stop;
+  a2.alpha = h->cfg.alpha;
+  a2.t = t;
+  a2.out_beam = beam_idx;
+  a2.out_tok = token_id;
+  a2.out_score = scores;
+  a2.out_done = done;
+  launch_k2(a2, h->wmax, h->stream);
+  rc = launch_status();
+  if (rc != BS_OK) return rc;
+  h->t = t;
+  return BS_OK;
+}
+
+int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
+  if (!h || !kv || !kv->planes || kv->n_planes < 1 || gen_len < 0) return BS_EINVAL;
+  if (kv->bytes_per_pos <= 0 || kv->row_stride <= 0 || kv->pos_stride <= 0 || kv->pos_offset < 0)
+    return BS_EINVAL;
+  if (h->t == 0) return BS_ESTATE;
+  if (gen_len == 0) return BS_OK;
+  const int64_t base_off = kv->pos_offset * kv->pos_stride;
+  bool a16 = (kv->bytes_per_pos % 16 == 0) && (kv->row_stride % 16 == 0) &&
+             (kv->pos_stride % 16 == 0) && (base_off % 16 == 0);
+  bool a4 = (kv->bytes_per_pos % 4 == 0) && (kv->row_stride % 4 == 0) &&
+            (kv->pos_stride % 4 == 0) && (base_off % 4 == 0);
+  for (int i = 0; i < kv->n_planes; ++i) {
+    if (!kv->planes[i]) return BS_EINVAL;
+    a16 = a16 && ((uintptr_t)kv->planes[i] % 16 == 0);
+    a4 = a4 && ((uintptr_t)kv->planes[i] % 4 == 0);
+  }
+  if (!a4) return BS_EINVAL;
+  const int word = a16 ? 16 : 4;
+  const bool contig = kv->pos_stride == kv->bytes_per_pos;
+  K3Args a;
+  a.row_stride = kv->row_stride;
+  a.pos_stride = kv->pos_stride;
+  a.base_off = base_off;
+  a.words_per_pos = kv->bytes_per_pos / word;
+  a.words = (int64_t)gen_len * a.words_per_pos;
+  a.W = h->W;
+  a.plan = h->st.plan;
+  for (int p0 = 0; p0 < kv->n_planes; p0 += kMaxPlanesPerLaunch) {
+    const int np = kv->n_planes - p0 < kMaxPlanesPerLaunch ? kv->n_planes - p0
+                                                           : kMaxPlanesPerLaunch;
+    for (int i = 0; i < np; ++i) a.planes[i] = (char*)kv->planes[p0 + i];
+    launch_k3(a, h->wmax, word, contig, h->B, np, h->stream);
+    const int rc = launch_status();
+    if (rc != BS_OK) return rc;
+  }
+  return BS_OK;
+}
+
+int bs_finalize(bs_state* h, int32_t* tokens, int32_t* lengths, float* norm_scores) {
+  if (!h || !tokens || !lengths || !norm_scores) return BS_EINVAL;
+  if (h->t == 0) return BS_ESTATE;
+  K5Args a;
+  a.st = h->st;
+  a.B = h->B;
+  a.W = h->W;
+  a.T = h->T;
+  a.pad = h->cfg.pad_id;
+  a.R = h->cfg.num_return;
+  a.steps = h->t;
+  a.tokens = tokens;
+  a.lengths = lengths;
+  a.norms = norm_scores;
+  launch_k5(a, h->wmax, h->stream);
+  return launch_status();
+}
+
+int bs_last_selection(bs_state* h, int32_t* flat_idx, float* cand_score) {
+  if (!h || !flat_idx || !cand_score) return BS_EINVAL;
+  if (h->t == 0) return BS_ESTATE;
+  const size_t n = (size_t)h->rows;
+  if (hipMemcpyAsync(flat_idx, h->st.sel_j, n * 4, hipMemcpyDeviceToDevice, h->stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(cand_score, h->st.sel_c, n * 4, hipMemcpyDeviceToDevice, h->stream) !=
+          hipSuccess)
+    return BS_EDEVICE;
+  return BS_OK;
+}
+
+int bs_get_finished(bs_state* h, float* norm, float* raw, int32_t* len, int32_t* step,
+                    int32_t* rank, int32_t* count) {
+  if (!h || !norm || !raw || !len || !step || !rank || !count) return BS_EINVAL;
+  const size_t n = (size_t)h->rows * 4;
+  const hipMemcpyKind k = hipMemcpyDeviceToDevice;
+  if (hipMemcpyAsync(norm, h->st.hnorm, n, k, h->stream) != hipSuccess ||
+      hipMemcpyAsync(raw, h->st.hraw, n, k, h->stream) != hipSuccess ||
+      hipMemcpyAsync(len, h->st.hlen, n, k, h->stream) != hipSuccess ||
+      hipMemcpyAsync(step, h->st.hstep, n, k, h->stream) != hipSuccess ||
+      hipMemcpyAsync(rank, h->st.hrank, n, k, h->stream) != hipSuccess ||
+      hipMemcpyAsync(count, h->st.hcount, (size_t)h->B * 4, k, h->stream) != hipSuccess)
+    return BS_EDEVICE;
+  return BS_OK;
+}
+
+int bs_steps_taken(const bs_state* h) { return h ? h->t : BS_EINVAL; }
+
+void bs_destroy(bs_state* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->stream);
+  (void)hipFree(h->block);
+  free(h);
+}
+
+int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dtype,
+                     void* hip_stream, bs_verify_state** out) {
+  if (!out) return BS_EINVAL;
+  *out = nullptr;
+  if (batch < 1 || k < 1 || k > 64 || vocab < 1) return BS_EINVAL;
+  if (logits_dtype != BS_F32 && logits_dtype != BS_BF16) return BS_EINVAL;
+  bs_verify_state* h = (bs_verify_state*)calloc(1, sizeof(bs_verify_state));
+  if (!h) return BS_ENOMEM;
+  h->stream = (hipStream_t)hip_stream;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    free(h);
+    return BS_EDEVICE;
+  }
+  h->B = batch;
+  h->k = k;
+  h->V = vocab;
+  h->dtype = logits_dtype;
+  h->ept = choose_ept(batch * k, vocab, 0);
+  h->tile = kThreads * h->ept;
+  h->tiles = (vocab + h->tile - 1) / h->tile;
+  const size_t pt = (size_t)batch * k * h->tiles;
+  if (hipMalloc(&h->block, 2 * align_up(pt * 4)) != hipSuccess) {
+    (void)hipGetLastError();
+    free(h);
+    return BS_ENOMEM;
+  }
+  h->px = (float*)h->block;
+  h->pv = (int*)((char*)h->block + align_up(pt * 4));
+  *out = h;
+  return BS_OK;
+}
+
+int bs_verify(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
+              const int32_t* proposals, int32_t* accept_len, int32_t* argmax) {
+  if (!h || !logits || !proposals || !accept_len || !argmax) return BS_EINVAL;
+  if (row_stride_elems < h->V) return BS_EINVAL;
+  const int esize = h->dtype == BS_BF16 ? 2 : 4;
+  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((row_stride_elems * esize) % 16 == 0);
+  K4Args a;
+  a.logits = logits;
+  a.stride = row_stride_elems;
+  a.V = h->V;
+  a.tile = h->tile;
+  a.tiles = h->tiles;
+  a.k = h->k;
+  a.B = h->B;
+  a.px = h->px;
+  a.pv = h->pv;
+  a.proposals = proposals;
+  a.accept = accept_len;
+  a.argmax = argmax;
+  dim3 grid(h->tiles, h->B * h->k);
+  if (h->dtype == BS_BF16) launch_k4_e<uint16_t>(a, h->ept, aligned, grid, h->stream);
+  else launch_k4_e<float>(a, h->ept, aligned, grid, h->stream);
+  int rc = launch_status();
+  if (rc != BS_OK) return rc;
+  hipLaunchKernelGGL(k4_accept, dim3(h->B), dim3(64), 0, h->stream, a);
+  return launch_status();
+}
+
+void bs_verify_destroy(bs_verify_state* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->stream);
+  (void)hipFree(h->block);
+  free(h);
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+/*
+ * beamstep.h -- C ABI of libbeamstep.so, a batched beam-search decode step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of beam search, as described in "llm_internals" section
+ * 9.2.2 (the four sub-steps expand, score, prune, finalize) and in the
+ * batched section of "Transformers中的Beam Search高效实现" (rows b*W+w,
+ * running scores initialised to [0, -inf, ...] per item, a finished set of
+ * capacity W per item, early stopping), followed by the KV-cache reorder by
+ * beam_idx ("llm_internals" 9.2.2, KV-cache paragraph) and, separately, the
+ * verify sub-step of blockwise parallel decoding ("Blockwise Parallel
+ * Decoding for Deep Autoregressive Models", section 3).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers documented as "device" point to memory the caller allocated on
+ *     the GPU the handle was created on (for example torch tensors); the
+ *     library never frees them. Pointers documented as "host" are plain CPU
+ *     memory, read during the call only.
+ *   - Every call is enqueued on the handle's HIP stream and returns without
+ *     waiting for the GPU, except where stated. Results are valid once the
+ *     stream reaches them.
+ *   - Every call returns a bs_status. Arguments are validated before any work
+ *     is enqueued; a call that returns an error has enqueued nothing and left
+ *     the handle unchanged. BS_EDEVICE reports a HIP error seen at launch.
+ *   - A handle is not thread-safe; use one handle per stream.
+ *   - Logits must not contain NaN or +inf (behaviour is undefined); -inf is
+ *     allowed and means "impossible token".
+ */
+#ifndef BEAMSTEP_H
+#define BEAMSTEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BS_OK = 0,
+    BS_EINVAL = -1,  /* invalid argument or configuration            */
+    BS_ENOMEM = -2,  /* device allocation failed (bs_create only)    */
+    BS_EDEVICE = -3, /* HIP runtime error                            */
+    BS_ESTATE = -4   /* call not valid in the handle's current state */
+} bs_status;
+
+typedef enum { BS_F32 = 0, BS_BF16 = 1 } bs_dtype;
+
+/* Length normalisation, "llm_internals" 9.2.3: the normalised score of a
+ * finished hypothesis is log P / lp(|y|) with
+ *   BS_LP_GNMT: lp = ((5 + |y|) / 6)^alpha
+ *   BS_LP_POW : lp = |y|^alpha        (Hugging Face's length_penalty)
+ *   BS_LP_NONE: lp = 1
+ * |y| counts the generated tokens whose log-probabilities are in the score,
+ * EOS included. lp is evaluated in double; the normalised score is
+ * fp32(raw / lp). */
+typedef enum { BS_LP_NONE = 0, BS_LP_GNMT = 1, BS_LP_POW = 2 } bs_lp;
+
+/* When an item stops ("llm_internals" 9.2.2, "when to stop"; the is_done
+ * test of the batched section). Checked once per item per step, after the
+ * step's EOS hypotheses entered the finished set; an item with no live beam
+ * left is always done.
+ *   BS_STOP_TRUE     : done once W hypotheses are finished.
+ *   BS_STOP_HEURISTIC: done once W are finished and the worst kept normalised
+ *                      score >= fp32(best / lp(t)), best being the score of
+ *                      the step's rank-0 selection and t the step.
+ *   BS_STOP_NEVER    : done once W are finished and the worst kept normalised
+ *                      score >= the best any live beam can still reach:
+ *                      s / lp(max_steps) when alpha > 0 and s <= 0, else
+ *                      s / lp(t), s being the best live score. */
+typedef enum { BS_STOP_TRUE = 0, BS_STOP_HEURISTIC = 1, BS_STOP_NEVER = 2 } bs_stop;
+
+typedef struct {
+    int32_t batch;        /* B >= 1                                        */
+    int32_t beam;         /* W, 1..16                                      */
+    int32_t vocab;        /* V >= 1, with W*V < 2^31                       */
+    int32_t max_steps;    /* T >= 1: decode steps, the longest hypothesis  */
+    int32_t eos_id;       /* EOS token, or < 0 for none                    */
+    int32_t pad_id;       /* token reported for dead slots and padding     */
+    int32_t logits_dtype; /* bs_dtype                                      */
+    int32_t lp;           /* bs_lp                                         */
+    double alpha;         /* length-penalty exponent                       */
+    int32_t stop;         /* bs_stop                                       */
+    int32_t num_return;   /* hypotheses returned per item, 1..W            */
+    int32_t tile_elems;   /* logits per thread in the streaming pass:
+                             16, 32 or 64; 0 picks one from B, W, V       */
+} bs_config;
+
+typedef struct bs_state bs_state;
+
+/* Creates a handle for one batched search on the current HIP device and
+ * allocates, once, every buffer the search needs at its maximum shapes
+ * (running scores, per-tile partial results, finished sets, backpointers
+ * [T][B][W], done flags, the reorder plan), following the static-shape
+ * memory reuse of the LightSeq article ("动态显存复用"): no later call
+ * allocates. Initialises the running scores to [0, -inf, ..., -inf] per item.
+ *   cfg        host, read only
+ *   hip_stream a hipStream_t (NULL: the null stream) that every later call on
+ *              this handle is ordered on
+ *   out        host; receives the handle
+ * Errors: BS_EINVAL (bad config), BS_ENOMEM, BS_EDEVICE. Synchronises the
+ * stream before returning. */
+int bs_create(const bs_config *cfg, void *hip_stream, bs_state **out);
+
+/* Starts a new search on the same handle: scores back to [0, -inf, ...],
+ * finished sets emptied, done flags cleared, step counter to 0. */
+int bs_reset(bs_state *h);
+
+/* One decode step t = (steps taken) + 1, "llm_internals" 9.2.2:
+ *   expand   lse_r = ln sum_v exp(x[r][v]) per live row r (fp32 arithmetic,
+ *            logits read once; the log-probabilities are never stored),
+ *   score    cand = fp32(s_r + fp32(x[r][v] - lse_r)) for j = w*V + v,
+ *   prune    the W best candidates of each item over its W*V flattened
+ *            candidates, ordered by (cand desc, j asc); parent w = j / V,
+ *            token = j % V (integer quotient and remainder),
+ *   finalize in rank order, an EOS selection enters the item's finished set
+ *            with |y| = t; every other selection becomes the next live slot.
+ *            Live slots are compacted in rank order; remaining slots are dead
+ *            (score -inf). Then the stop rule runs (see bs_stop).
+ * Rows of items that are done, and dead rows (score -inf), are not read, so
+ * their logits may hold anything.
+ *   logits           device, [B*W][row_stride_elems] of fp32 or bf16 (as
+ *                    configured); row r = b*W + w; only the first V of each
+ *                    row are read
+ *   row_stride_elems >= V
+ *   beam_idx         device int32 [B][W], written: local parent slot
+ *                    (0..W-1) of each new slot; own slot for dead slots and
+ *                    for items already done before this step
+ *   token_id         device int32 [B][W], written: the new token; pad_id for
+ *                    dead slots and done items
+ *   scores           device fp32 [B][W], written: the new running score; -inf
+ *                    for dead slots and done items
+ *   done             device uint8 [B], written: 1 if the item is done after
+ *                    this step
+ * Errors: BS_EINVAL (NULL pointer, stride < V); BS_ESTATE if max_steps steps
+ * were already taken; BS_EDEVICE. */
+int bs_step(bs_state *h, const void *logits, int64_t row_stride_elems,
+            int32_t *beam_idx, int32_t *token_id, float *scores, uint8_t *done);
+
+/* KV-cache layout for bs_reorder_kv: n_planes planes (one per layer and K or
+ * V), each holding rows b*W+w of positions of bytes_per_pos contiguous bytes. */
+typedef struct {
+    int32_t n_planes;        /* >= 1                                          */
+    void *const *planes;     /* host array of n_planes device pointers        */
+    int64_t row_stride;      /* bytes between row r and row r+1 of a plane    */
+    int64_t pos_stride;      /* bytes between position p and p+1 of a row     */
+    int64_t pos_offset;      /* first position the reorder touches: a prompt
+                                kept before it is shared and never moved      */
+    int64_t bytes_per_pos;   /* bytes of one position of one row              */
+} bs_kv_desc;
+
+/* The cache reorder that follows the last bs_step ("llm_internals" 9.2.2,
+ * KV-cache paragraph: a new slot reads its parent's cache, and a parent chosen
+ * by several slots is copied to each). For every item not done after that
+ * step and every live slot i whose parent p = beam_idx[b][i] differs from i,
+ * positions [pos_offset, pos_offset + gen_len) of row b*W+i of every plane
+ * become what row b*W+p held before the call, bit for bit. Rows of slots that
+ * keep their parent, dead slots and done items are not touched. Every
+ * distinct parent is read once per position; the copy is in place and safe
+ * for swaps and cycles.
+ *   kv       host descriptor; planes are device pointers
+ *   gen_len  number of positions to move (>= 0; 0 is a no-op)
+ * Requires bytes_per_pos, row_stride, pos_stride, pos_offset*pos_stride and
+ * every plane address to be multiples of 4 bytes (16 for the fast path).
+ * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
+int bs_reorder_kv(bs_state *h, const bs_kv_desc *kv, int32_t gen_len);
+
+/* Final selection (batched section of "Transformers中的Beam Search高效实现",
+ * after the decode loop): every live beam of an item that is not done joins
+ * a copy of its finished set with |y| = steps taken; the best num_return
+ * hypotheses per item, ordered by (normalised score desc, step asc, rank
+ * asc), are written out. Does not change the handle; may be called again.
+ *   tokens       device int32 [B][num_return][max_steps]: the generated
+ *                tokens (EOS included when the hypothesis ended with it),
+ *                pad_id after the end
+ *   lengths      device int32 [B][num_return]: |y|; 0 for a missing entry
+ *   norm_scores  device fp32 [B][num_return]: normalised score; -inf for a
+ *                missing entry
+ * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
+int bs_finalize(bs_state *h, int32_t *tokens, int32_t *lengths, float *norm_scores);
+
+/* The ranked selection of the last bs_step, before compaction ("prune"
+ * output): flat index j (= parent*V + token) and fp32 candidate score, for
+ * ranks 0..W-1 of each item; j = -1 and score -inf where an item had fewer
+ * than W finite candidates or was already done.
+ *   flat_idx  device int32 [B][W];  cand_score  device fp32 [B][W]
+ * Errors: BS_EINVAL; BS_ESTATE before the first bs_step. */
+int bs_last_selection(bs_state *h, int32_t *flat_idx, float *cand_score);
+
+/* Each item's finished set as it stands (storage order, unsorted):
+ *   norm, raw  device fp32 [B][W]; len, step, rank  device int32 [B][W];
+ *   count      device int32 [B]  (entries at index >= count are undefined) */
+int bs_get_finished(bs_state *h, float *norm, float *raw, int32_t *len,
+                    int32_t *step, int32_t *rank, int32_t *count);
+
+/* Steps taken since bs_create or bs_reset (host value, no GPU work). */
+int bs_steps_taken(const bs_state *h);
+
+/* Frees the handle's device buffers after synchronising its stream. */
+void bs_destroy(bs_state *h);
+
+/* Blockwise-parallel verify ("Blockwise Parallel Decoding", section 3, the
+ * verify sub-step, and Figure 1): for each item b and position i < k,
+ * argmax[b][i] is the first index of the largest logit of row b*k+i (greedy
+ * needs no softmax, "llm_internals" 9.2.1), and accept_len[b] is the largest
+ * k' <= k with proposals[b][i] == argmax[b][i] for every i < k'. When
+ * proposals[b][0] is the base model's own greedy token, accept_len >= 1. */
+typedef struct bs_verify_state bs_verify_state;
+
+/* Allocates the per-tile partial results for logits [B][k][V] once.
+ *   batch >= 1, k in 1..64, vocab >= 1; logits_dtype a bs_dtype. */
+int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dtype,
+                     void *hip_stream, bs_verify_state **out);
+
+/*   logits      device [B*k][row_stride_elems] (row b*k+i), fp32 or bf16
+ *   proposals   device int32 [B][k]
+ *   accept_len  device int32 [B], written
+ *   argmax      device int32 [B][k], written
+ * Errors: BS_EINVAL (NULL pointer, stride < V); BS_EDEVICE. */
+int bs_verify(bs_verify_state *h, const void *logits, int64_t row_stride_elems,
+              const int32_t *proposals, int32_t *accept_len, int32_t *argmax);
+
+void bs_verify_destroy(bs_verify_state *h);
+
+/* Static description of a status code. */
+const char *bs_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAMSTEP_H */

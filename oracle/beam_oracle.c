@@ -493,13 +493,16 @@ int or_step(or_search *o, const void *logits, int64_t row_stride,
  * current length, then writes the best num_return hypotheses per item in
  * finished-set order: tokens [B][R][T] pad-filled (EOS included when the
  * hypothesis ended with it), lengths [B][R], normalised scores [B][R].
- * Missing entries get length 0, score -inf, all pad. Runs once. */
+ * Missing entries get length 0, score -inf, all pad. Requires at least one
+ * step; adding the live beams happens once. */
 int or_finish(or_search *o, int num_return, int32_t *tokens, int32_t *lengths,
               float *norms)
 {
     int B = o->B, W = o->W, T = o->T;
     if (num_return < 1 || num_return > W)
         return -1;
+    if (o->t == 0)
+        return -4; /* the final selection follows at least one decode step */
     if (!o->finished) {
         for (int b = 0; b < B; ++b) {
             if (o->done[b])

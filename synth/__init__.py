@@ -129,6 +129,7 @@ class Workload:
     zipf_s: float          # 0: no Zipf bias
     eos_ramp: float        # EOS bias reaches this value at step ramp_steps (0: none)
     ramp_steps: int
+    eos_start: float       # EOS bias at step 0 when it ramps
     eos_in_zipf: bool      # whether the EOS id also carries the Zipf term
     lp: str                # "none" | "gnmt" | "pow"
     alpha: float
@@ -170,19 +171,19 @@ class Workload:
 
 WORKLOADS = {
     # toy: B=3, W=2, V=6, EOS 5, fp32 N(0,1) per step, 10 steps, GNMT 0.6
-    "toy": Workload("toy", 3, 2, 6, 10, 5, -1, "f32", 1.0, 0.0, 0.0, 1, True,
+    "toy": Workload("toy", 3, 2, 6, 10, 5, -1, "f32", 1.0, 0.0, 0.0, 1, 0.0, True,
                     "gnmt", 0.6, "heuristic", 1, 1, 2, 4, "f32", 0, 1001, 1),
     # Transformer-base MT shape
     "tbase": Workload("tbase", 32, 4, 32000, 128, 1, -1, "f32", 2.0, 1.1, 6.0,
-                      100, False, "gnmt", 0.6, "heuristic", 1, 6, 8, 64, "f32",
+                      100, -8.0, False, "gnmt", 0.6, "heuristic", 1, 6, 8, 64, "f32",
                       0, 1002, 128),
     # Llama-3-8B shape: bf16 logits, EOS = V-1 under the Zipf term
     "llama3_8b": Workload("llama3_8b", 8, 4, 128256, 200, 128255, -1, "bf16",
-                          3.0, 1.0, 0.0, 1, True, "pow", 1.0, "true", 1, 32,
+                          3.0, 1.0, 0.0, 1, 0.0, True, "pow", 1.0, "true", 1, 32,
                           8, 128, "bf16", 1000, 1003, 64),
     # wide-beam stress
     "wide": Workload("wide", 16, 16, 250000, 256, 249999, -1, "f32", 2.0, 1.2,
-                     0.0, 1, True, "gnmt", 0.7, "heuristic", 1, 6, 16, 64,
+                     0.0, 1, 0.0, True, "gnmt", 0.7, "heuristic", 1, 6, 16, 64,
                      "f32", 0, 1005, 3),
 }
 
@@ -198,7 +199,8 @@ def token_bias(wl: Workload, step: int) -> np.ndarray:
     if wl.eos_id >= 0 and not wl.eos_in_zipf:
         bias[wl.eos_id] = 0.0
     if wl.eos_id >= 0 and wl.eos_ramp:
-        bias[wl.eos_id] += wl.eos_ramp * min(step, wl.ramp_steps) / wl.ramp_steps
+        f = min(step, wl.ramp_steps) / wl.ramp_steps
+        bias[wl.eos_id] += wl.eos_start + (wl.eos_ramp - wl.eos_start) * f
     return bias
 
 

@@ -1,0 +1,79 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import beam_search_step_amd as bs
+
+
+def test_library_exports_every_declared_function():
+    names = bs.declared_functions()
+    assert len(names) == 13
+    lib = bs.library()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_exports_match_header_exactly():
+    out = subprocess.run(["nm", "-D", "--defined-only", bs.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T bs_" in ln})
+    assert exported == bs.declared_functions()
+
+
+def test_library_is_built_for_gfx950():
+    with open(bs.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_strerror():
+    assert bs.bs_strerror(bs.BS_OK) == "ok"
+    assert bs.bs_strerror(bs.BS_EINVAL) == "invalid argument"
+    assert bs.bs_strerror(bs.BS_ESTATE).startswith("call not valid")
+    assert bs.bs_strerror(12345) == "unknown status"
+
+
+def _cfg(**kw):
+    base = dict(batch=2, beam=4, vocab=100, max_steps=8, eos_id=3, pad_id=-1, logits_dtype=0,
+                lp=1, alpha=0.6, stop=1, num_return=1, tile_elems=0)
+    base.update(kw)
+    return bs.bs_config(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=0), dict(beam=0), dict(beam=17), dict(vocab=0), dict(max_steps=0),
+    dict(logits_dtype=2), dict(lp=3), dict(stop=3), dict(num_return=0), dict(num_return=5),
+    dict(tile_elems=8), dict(alpha=float("nan")), dict(beam=16, vocab=2 ** 27),
+])
+def test_create_rejects_invalid_config(kw):
+    h = ctypes.c_void_p(123)
+    rc = bs.library().bs_create(ctypes.byref(_cfg(**kw)), None, ctypes.byref(h))
+    assert rc == bs.BS_EINVAL
+    assert h.value is None
+
+
+def test_null_arguments_are_rejected():
+    L = bs.library()
+    assert L.bs_create(None, None, None) == bs.BS_EINVAL
+    assert L.bs_step(None, None, 0, None, None, None, None) == bs.BS_EINVAL
+    assert L.bs_reorder_kv(None, None, 0) == bs.BS_EINVAL
+    assert L.bs_finalize(None, None, None, None) == bs.BS_EINVAL
+    assert L.bs_reset(None) == bs.BS_EINVAL
+    assert L.bs_verify(None, None, 0, None, None, None) == bs.BS_EINVAL
+    h = ctypes.c_void_p()
+    assert L.bs_verify_create(0, 8, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
+    assert L.bs_verify_create(2, 65, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
+    L.bs_destroy(None)
+    L.bs_verify_destroy(None)
+
+
+def test_config_struct_layout_matches_header():
+    # offsets of the C struct on x86-64: eight int32, a double, three int32
+    assert ctypes.sizeof(bs.bs_config) == 56
+    assert bs.bs_config.alpha.offset == 32
+    assert bs.bs_config.tile_elems.offset == 48
+    assert ctypes.sizeof(bs.bs_kv_desc) == 48

@@ -1,0 +1,358 @@
+"""Parity of the HIP library with the CPU oracle on an MI355X.
+
+Every test calls the library through its C ABI (the ctypes binding) and
+compares element by element with the oracle on the same seeded inputs:
+selection, beam_idx, token_id, running scores, done flags and finished sets
+each step (teacher-forced, see tests/parity.py), final hypotheses, and the KV
+cache bit for bit. Sizes: the toy workload in full; the other workloads at
+their full B, W and V with a sample of batch items followed by the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import Report, compare_final, run_stepwise, same_float, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import beam_search_step_amd as bs
+    bs.library()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    torch.cuda.set_device(0)
+    return torch.device("cuda", 0)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked example on the GPU
+# ---------------------------------------------------------------------------
+def test_table_9_5_tree_and_kv_swap(dev):
+    import beam_search_step_amd as bs
+    g = bs.BeamSearch(1, 2, 3, 2, lp="none", alpha=0.0)
+    s1 = np.log(np.array([[0.5, 0.4, 0.1], [0.5, 0.4, 0.1]])).astype(np.float32)
+    s2 = np.log(np.array([[0.40, 0.35, 0.25], [0.90, 0.06, 0.04]])).astype(np.float32)
+    bi, tk, sc, dn = g.step(torch.from_numpy(s1).to(dev))
+    assert bi.tolist() == [[0, 0]] and tk.tolist() == [[0, 1]]
+    kv = [torch.tensor([[[11, 12, 13, 14]], [[21, 22, 23, 24]]], dtype=torch.int32,
+                       device=dev) for _ in range(2)]
+    bi, tk, sc, dn = g.step(torch.from_numpy(s2).to(dev))
+    assert bi.tolist() == [[1, 0]] and tk.tolist() == [[0, 0]]   # B x, A x
+    np.testing.assert_allclose(sc.cpu().numpy()[0], [math.log(0.36), math.log(0.2)], atol=1e-5)
+    assert abs(sc[0, 0].item() - (-1.022)) < 1e-3 and abs(sc[0, 1].item() - (-1.609)) < 1e-3
+    g.reorder_kv(kv, 1)
+    for p in kv:   # beam_idx = [1, 0] is a swap: the rows trade places in place
+        assert p.cpu().tolist() == [[[21, 22, 23, 24]], [[11, 12, 13, 14]]]
+    tok, ln, nm = g.finalize()
+    assert tok.cpu().tolist() == [[[1, 0]]] and ln.tolist() == [[2]]
+    g.close()
+
+
+def test_w1_is_greedy_argmax(dev):
+    """W=1 is greedy search: the token is the first index of the row maximum."""
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["tbase"].replace(batch=16, beam=1, eos_id=-1, max_steps=6)
+    g = bs.BeamSearch.for_workload(wl)
+    for t in range(1, 7):
+        lg = synth.logits(wl, t)
+        bi, tk, sc, dn = g.step(torch.from_numpy(lg).to(dev))
+        assert np.array_equal(tk.cpu().numpy()[:, 0], lg.argmax(-1))
+        assert (bi.cpu().numpy() == 0).all()
+    g.close()
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+def test_toy_workload_full(dev):
+    wl = synth.WORKLOADS["toy"]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=2)
+    compare_final(g, ref, range(wl.batch), wl.num_return, "toy")
+    log(f"toy: {rep}")
+    g.close()
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("stop", ["heuristic", "true", "never"])
+def test_toy_variants_with_frequent_eos(dev, seed, stop):
+    wl = synth.WORKLOADS["toy"].replace(seed=seed, eos_in_zipf=False, eos_ramp=2.0,
+                                        ramp_steps=3, stop=stop, num_return=2)
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1)
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"toy {seed} {stop}")
+    g.close()
+
+
+@pytest.mark.parametrize("W,V,lp", [(1, 7, "gnmt"), (3, 37, "pow"), (5, 3, "none"),
+                                    (8, 1000, "gnmt"), (16, 2, "pow"), (16, 9000, "gnmt")])
+def test_small_shapes(dev, W, V, lp):
+    """Odd V (unaligned rows, ragged tiles), V < W (dead slots), W up to 16."""
+    wl = synth.WORKLOADS["toy"].replace(batch=5, beam=W, vocab=V, eos_id=min(2, V - 1),
+                                        eos_in_zipf=False, eos_ramp=1.0, ramp_steps=4,
+                                        lp=lp, alpha=0.8, max_steps=9, seed=40 + W,
+                                        num_return=min(W, 3))
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1)
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"W={W} V={V}")
+    g.close()
+
+
+def test_transformer_base_sampled_items(dev):
+    """B=32, W=4, V=32000 fp32 with the EOS ramp, all 128 steps; the oracle
+    follows items 0, 13 and 31."""
+    wl = synth.WORKLOADS["tbase"]
+    items = [0, 13, 31]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=2)
+    compare_final(g, ref, items, wl.num_return, "tbase")
+    log(f"tbase: {rep}")
+    assert rep.compared >= 3 * 20
+    g.close()
+
+
+def test_llama3_8b_sampled_items(dev):
+    """B=8, W=4, V=128256 bf16 (ties are common), 12 steps, items 0 and 5,
+    KV planes of 2 KiB per position."""
+    wl = synth.WORKLOADS["llama3_8b"]
+    rep, g, ref = run_stepwise(wl, 12, dev, items=[0, 5], kv_planes=2)
+    log(f"llama3_8b: {rep}")
+    g.close()
+
+
+def test_llama3_8b_with_reachable_eos(dev):
+    """The Llama-shaped workload with EOS = 1 outside the Zipf term and a
+    rising EOS bias, so that the EOS path and early stopping run at V=128256."""
+    wl = synth.WORKLOADS["llama3_8b"].replace(batch=3, eos_id=1, eos_in_zipf=False,
+                                              eos_ramp=14.0, ramp_steps=10, max_steps=20)
+    rep, g, ref = run_stepwise(wl, 20, dev, kv_planes=1)
+    compare_final(g, ref, range(wl.batch), wl.num_return, "llama3 eos")
+    assert any(len(ref.hyps(b)) for b in range(wl.batch)), "no EOS was selected"
+    g.close()
+
+
+@pytest.mark.parametrize("tile_elems", [0, 16])
+def test_wide_beam_sampled_items(dev, tile_elems):
+    """B=16, W=16, V=250000 fp32 (top-16 of 4.0M per item), 3 steps, items 3
+    and 12. tile_elems=16 gives 62 tiles per row, so the merge runs in several
+    batches."""
+    wl = synth.WORKLOADS["wide"]
+    rep, g, ref = run_stepwise(wl, 3, dev, items=[3, 12], kv_planes=1, tile_elems=tile_elems)
+    log(f"wide tile={tile_elems}: {rep}")
+    g.close()
+
+
+def test_verify_full_size(dev):
+    import beam_search_step_amd as bs
+    cfg = synth.VERIFY
+    ver = bs.Verifier(cfg["batch"], cfg["k"], cfg["vocab"])
+    accs = []
+    for call in range(2):
+        lg, prop = synth.verify_inputs(cfg["batch"], cfg["k"], cfg["vocab"], cfg["seed"],
+                                       call=call)
+        acc, am = ver(torch.from_numpy(lg).to(dev), torch.from_numpy(prop).to(dev))
+        oacc, oam = oracle.verify(lg, prop)
+        assert np.array_equal(am.cpu().numpy(), oam)
+        assert np.array_equal(acc.cpu().numpy(), oacc)
+        assert (oacc >= 1).all()
+        accs.append(oacc.mean())
+    log(f"verify: mean accepted {np.mean(accs):.3f} (expected about 2.458)")
+    assert 1.8 < np.mean(accs) < 3.2
+    ver.close()
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_verify_edge_cases(dev):
+    import beam_search_step_amd as bs
+    rng = np.random.default_rng(9)
+    for (B, k, V, dtype) in [(3, 5, 9, "f32"), (2, 1, 4097, "f32"), (4, 64, 300, "bf16"),
+                             (1, 8, 70001, "bf16")]:
+        x = rng.integers(-3, 3, size=(B, k, V)).astype(np.float32)   # many ties
+        x[0, 0] = -np.inf                                           # an all -inf row
+        if dtype == "bf16":
+            x = synth.f32_to_bf16_bits(x)
+        am_ref = synth.widen(dtype, x).argmax(-1)
+        prop = am_ref.astype(np.int32).copy()
+        prop[-1, k // 2] = (prop[-1, k // 2] + 1) % V
+        ver = bs.Verifier(B, k, V, dtype)
+        acc, am = ver(to_device(x, dev), torch.from_numpy(prop).to(dev))
+        oacc, oam = oracle.verify(x, prop, dtype)
+        assert np.array_equal(am.cpu().numpy(), oam) and np.array_equal(oam, am_ref)
+        assert np.array_equal(acc.cpu().numpy(), oacc)
+        ver.close()
+
+
+def test_row_stride_larger_than_vocab(dev):
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["tbase"].replace(batch=3, vocab=5000, max_steps=3)
+    g = bs.BeamSearch.for_workload(wl)
+    ref = oracle.Search.for_workload(wl)
+    for t in (1, 2, 3):
+        lg = synth.logits(wl, t)
+        pad = np.full((wl.rows, 5003), 99.0, np.float32)   # junk after column V
+        pad[:, :5000] = lg
+        dpad = torch.from_numpy(pad).to(dev)
+        bi, tk, sc, dn = g.step(dpad[:, :5000])             # stride 5003, unaligned rows
+        obi, otk, osc, odn = ref.step(lg)
+        assert np.array_equal(bi.cpu().numpy(), obi) and np.array_equal(tk.cpu().numpy(), otk)
+        assert np.allclose(sc.cpu().numpy(), osc, atol=2e-5, rtol=0)
+    g.close()
+
+
+def test_massive_ties_and_minus_inf_rows(dev):
+    """Constant rows (every logit tied, more ties than the candidate list
+    holds), rows that are all -inf, and rows with a few finite logits."""
+    wl = synth.WORKLOADS["tbase"].replace(batch=4, vocab=20000, eos_id=-1, max_steps=3,
+                                          name="ties")
+
+    def logits_fn(t):
+        lg = synth.logits(wl, t)
+        lg[0:4] = 0.5                       # item 0: every row constant
+        lg[5] = -np.inf                     # item 1, row 1: no candidates
+        lg[8:12] = -np.inf                  # item 2: only three finite logits
+        lg[8, [7, 300, 19999]] = [1.0, 2.0, 1.0]
+        lg[13, :] = np.float32(3.0)         # item 3, row 1: constant, high
+        return lg
+
+    rep, g, ref = run_stepwise(wl, 3, dev, logits_fn=logits_fn, kv_planes=1)
+    compare_final(g, ref, range(wl.batch), 1, "ties")
+    g.close()
+
+
+def test_all_eos_step_and_calls_after_done(dev):
+    import beam_search_step_amd as bs
+    B, W, V, eos = 2, 3, 50, 7
+    g = bs.BeamSearch(B, W, V, 5, eos_id=eos, lp="gnmt", alpha=0.6, stop="heuristic")
+    ref = oracle.Search(B, W, V, 5, eos_id=eos, lp="gnmt", alpha=0.6, stop="heuristic")
+    lg = np.full((B * W, V), -5.0, np.float32)
+    lg[:, eos] = 5.0                      # EOS dominates every row
+    lg[3:, eos] = -5.0                    # ... except for item 1
+    lg[3:, 11] = 4.0
+    for t in range(1, 6):
+        bi, tk, sc, dn = g.step(torch.from_numpy(lg).to(dev))
+        obi, otk, osc, odn = ref.step(lg)
+        assert np.array_equal(bi.cpu().numpy(), obi) and np.array_equal(tk.cpu().numpy(), otk)
+        assert np.array_equal(dn.cpu().numpy().astype(bool), odn)
+        assert same_float(sc.cpu().numpy(), osc, ulps=64)
+    assert dn[0].item() == 1
+    with pytest.raises(bs.BeamStepError) as e:
+        g.step(torch.from_numpy(lg).to(dev))          # max_steps reached
+    assert e.value.status == bs.BS_ESTATE
+    tok, ln, nm = g.finalize()
+    otok, oln, onm = ref.finish(1)
+    assert np.array_equal(ln.cpu().numpy(), oln) and np.array_equal(tok.cpu().numpy(), otok)
+    g.close()
+
+
+def test_error_paths_on_device(dev):
+    import beam_search_step_amd as bs
+    g = bs.BeamSearch(2, 2, 10, 3)
+    x = torch.zeros((4, 10), device=dev)
+    with pytest.raises(bs.BeamStepError) as e:
+        g.finalize()
+    assert e.value.status == bs.BS_ESTATE
+    with pytest.raises(bs.BeamStepError) as e:
+        g.reorder_kv([torch.zeros((4, 3, 4), dtype=torch.int32, device=dev)], 1)
+    assert e.value.status == bs.BS_ESTATE
+    rc = bs.library().bs_step(g.h, x.data_ptr(), 9, g.beam_idx.data_ptr(),   # stride < V
+                              g.token_id.data_ptr(), g.scores.data_ptr(), g.done.data_ptr())
+    assert rc == bs.BS_EINVAL
+    g.step(x)
+    with pytest.raises(bs.BeamStepError) as e:   # 2-byte positions: not a multiple of 4
+        g.reorder_kv([torch.zeros((4, 3, 1), dtype=torch.int16, device=dev)], 1)
+    assert e.value.status == bs.BS_EINVAL
+    assert g.steps == 1
+    g.reset()
+    assert g.steps == 0
+    g.close()
+
+
+def test_reset_reproduces_and_is_deterministic(dev):
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["tbase"].replace(batch=8, max_steps=12)
+    g = bs.BeamSearch.for_workload(wl)
+    runs = []
+    for _ in range(2):
+        g.reset()
+        outs = []
+        for t in range(1, 13):
+            bi, tk, sc, dn = g.step(to_device(synth.logits(wl, t), dev))
+            outs.append([x.cpu().numpy().copy() for x in (bi, tk, sc, dn)])
+        outs.append([x.cpu().numpy() for x in g.finalize()])
+        runs.append(outs)
+    for a, b in zip(*runs):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    g.close()
+
+
+# ---------------------------------------------------------------------------
+# KV reorder: adversarial parent patterns
+# ---------------------------------------------------------------------------
+def _pattern_logits(V, spec):
+    """Step-2 logits: each row has a main token (logit 0) plus ``n`` tokens at
+    logit -8 that push the main token's log-prob down by ln(1 + n e^-8); all
+    other logits are -inf. spec[w] = (n, extra) where extra lists additional
+    (token, logit) pairs."""
+    x = np.full((len(spec), V), -np.inf, np.float32)
+    for w, (n, extra) in enumerate(spec):
+        x[w, 10 + w] = 0.0
+        if n:
+            x[w, 1000:1000 + n] = -8.0
+        for tok, val in extra:
+            x[w, tok] = val
+    return x
+
+
+PATTERNS = {
+    # (n per row, extra tokens) -> expected beam_idx for s ~ [-1, -1.5, -2, -2.5]
+    "swap": ([(3241, []), (0, []), (0, []), (0, [])], [1, 0, 2, 3]),
+    "cycle3": ([(10378, []), (0, []), (0, []), (5122, [])], [1, 2, 0, 3]),
+    "one_parent": ([(56890, []), (33330, []), (0, [(11, -0.01), (13, -0.02), (14, -0.03)]),
+                    (56890, [])], [2, 2, 2, 2]),
+    "shared_and_self": ([(0, [(11, -0.2)]), (0, [(12, -0.2)]), (56890, []), (56890, [])],
+                        [0, 0, 1, 1]),
+    "eos_dead_slot": ([(0, []), (0, [(5, 0.0)]), (0, []), (0, [])], None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PATTERNS))
+def test_kv_reorder_patterns(dev, name):
+    import beam_search_step_amd as bs
+    V, W, eos = 65536, 4, 5
+    spec, want = PATTERNS[name]
+    step1 = np.full((W, V), -np.inf, np.float32)
+    step1[0, 20:24] = [-1.0, -1.5, -2.0, -2.5]
+    if name == "eos_dead_slot":          # row 1's best token is EOS
+        spec = [(0, []), (0, []), (0, []), (0, [])]
+    step2 = _pattern_logits(V, spec)
+    if name == "eos_dead_slot":
+        step2[1, 11] = -np.inf
+        step2[1, eos] = 0.0
+    g = bs.BeamSearch(1, W, V, 4, eos_id=eos, lp="none", alpha=0.0, stop="never")
+    ref = oracle.Search(1, W, V, 4, eos_id=eos, lp="none", alpha=0.0, stop="never")
+    planes = [torch.from_numpy(np.arange(W * 3 * 8, dtype=np.int32).reshape(W, 3, 8) + 100 * p)
+              .to(dev) for p in range(3)]
+    host = [p.cpu().numpy() for p in planes]
+    for t, lg in ((1, step1), (2, step2)):
+        bi, tk, sc, dn = g.step(torch.from_numpy(lg).to(dev))
+        obi, otk, osc, odn = ref.step(lg)
+        assert np.array_equal(bi.cpu().numpy(), obi)
+        g.reorder_kv(planes, 3, pos_offset=0)
+        oracle.kv_reorder(host, obi, odn, 3)
+        for p, hp in zip(planes, host):
+            assert np.array_equal(p.cpu().numpy(), hp), f"{name} step {t}"
+    if want is not None:
+        assert obi[0].tolist() == want, f"construction gave {obi[0].tolist()}"
+    else:
+        assert osc[0, 3] == -np.inf and obi[0, 3] == 3   # dead slot keeps its row
+    g.close()
