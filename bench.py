@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8)
     ap.add_argument("--events", type=int, default=1,
-                    help="record HIP events around each kernel call (roofline)")
+                    help="record HIP events around each KV-reorder launch (roofline)")
+    ap.add_argument("--copy-reference", type=int, default=1,
+                    help="time a plain 1 GiB device copy after the timed region")
     return ap.parse_args()
 
 
@@ -55,9 +57,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the beam step "
-                                   "has no multi-GPU path in this library (see DESIGN.md "
-                                   "for how it would shard)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the beam-step "
+                                   "library has no multi-GPU path", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
@@ -93,27 +94,27 @@ def main():
     hist_dn = torch.empty((n_hist, B), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    # events are created before the timed region; per step, one pair brackets
+    # the KV-reorder launch on the library's stream
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps if args.events else 0)]
+    hist = [(hist_bi[i], hist_tk[i], hist_sc[i], hist_dn[i]) for i in range(n_hist)]
+
     def run(n, record):
-        ev = []
+        ts = []
         for i in range(n):
             t = (g.steps % T) + 1
             if t == 1 and g.steps:
                 g.reset()
-            lg = pool[i % args.pool]
-            h = i if record else 0
+            o = hist[i] if record else hist[0]
+            bs.bs_step(g.h, pool[i % args.pool], *o)
             if record and args.events:
-                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-                e0.record(stream)
-            bs.bs_step(g.h, lg, hist_bi[h], hist_tk[h], hist_sc[h], hist_dn[h])
-            if record and args.events:
-                e1.record(stream)
+                events[i][0].record(stream)
             bs.bs_reorder_kv(g.h, desc, t)
             if record and args.events:
-                e2.record(stream)
-                ev.append((t, e0, e1, e2))
-            elif record:
-                ev.append((t, None, None, None))
-        return ev
+                events[i][1].record(stream)
+            ts.append(t)
+        return ts
 
     # warmup (untimed), then the timed region
     g.reset()
@@ -121,7 +122,7 @@ def main():
     g.reset()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev = run(args.steps, True)
+    ts = run(args.steps, True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
@@ -132,7 +133,7 @@ def main():
     kv_bytes = []
     logit_bytes = []
     prev_live = np.zeros((B, W), bool)
-    for i, (t, *_rest) in enumerate(ev):
+    for i, t in enumerate(ts):
         if t == 1:
             prev_live = np.zeros((B, W), bool)
             prev_live[:, 0] = True
@@ -175,24 +176,74 @@ def main():
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if args.events:
-        d_step = np.array([a.elapsed_time(b) for _, a, b, _ in ev]) * 1e-3
-        d_kv = np.array([b.elapsed_time(c) for _, _, b, c in ev]) * 1e-3
+        d_kv = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
+        # between one step's reorder and the next: bs_step's two kernels
+        d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
+                           for i in range(1, len(events))]) * 1e-3
         ach = kv_bytes.sum() / d_kv.sum() / 1e9
         out["roofline"] = {
             "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+            "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+            "traffic": measured_traffic(kv_bytes.mean()),
             "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
         }
         out["step_kernels"] = {
-            "kernels": "k1_expand_select + k2_merge_finalize",
+            "kernels": "k1_expand_select + k2_merge_finalize (event gap between reorders)",
             "avg_us": 1e6 * d_step.mean(),
-            "alg_gbs": logit_bytes.sum() / d_step.sum() / 1e9,
+            "alg_gbs": logit_bytes[1:].sum() / d_step.sum() / 1e9,
         }
+    if args.copy_reference:
+        out["copy_reference"] = copy_reference(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n)
     out["input_generation_s"] = gen_s
     g.close()
     print(json.dumps(out))
+
+
+def copy_reference(torch, dev):
+    """A plain device copy of 1 GiB (torch's copy kernel): the practical
+    read+write HBM rate on this machine, for comparison with the KV reorder."""
+    n = 1 << 30
+    a = torch.empty(n // 2, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 5
+    return {"bytes_read_plus_written": 2 * n, "avg_us": us, "GBs": 2 * n / us / 1e3}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_kv_reorder_llama3_8b_traffic.json")
+
+
+def k3_source_hash():
+    """Hash of the KV-reorder kernel's source: counter readings are only used
+    while the kernel they were taken on is unchanged."""
+    import hashlib
+    src = open(os.path.join(ROOT, "beam_search_step_amd", "csrc", "beamstep.hip")).read()
+    i = src.index("// K3: in-place KV reorder")
+    j = src.index("// K4: blockwise verify")
+    return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
+
+
+def measured_traffic(alg_bytes_per_launch):
+    """HBM bytes per KV-reorder launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
+    None when there is none for the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("k3_source_sha256_16") != k3_source_hash():
+        return None
+    return d.get("bytes_per_launch")
 
 
 def cpu_baseline(wl, n_steps, bpp, planes_n):
