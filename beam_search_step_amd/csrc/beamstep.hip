@@ -814,9 +814,11 @@ __global__ __launch_bounds__(kThreads) void k3_kv_reorder(K3Args a) {
       const int cnt = plan[2 + kMaxBeam + q];
       for (int u = 0; u < cnt; ++u, ++d) {
         char* dst = base + (row0 + plan[2 + 2 * kMaxBeam + d]) * a.row_stride;
+        // streaming stores: the moved rows are not read again by this launch,
+        // and keeping them out of the caches measured ~10% faster end to end
 #pragma unroll
         for (int k = 0; k < NP; ++k)
-          if (ok[k]) *reinterpret_cast<WT*>(dst + off[k]) = v[k][q];
+          if (ok[k]) __builtin_nontemporal_store(v[k][q], reinterpret_cast<WT*>(dst + off[k]));
       }
     }
   }
