@@ -94,6 +94,73 @@ __device__ __forceinline__ float wave_sum(float s) {
   return s;
 }
 
+// Candidate keys packed into one unsigned 64-bit word so that a plain unsigned
+// maximum picks (score desc, index asc): the score's bits, mapped to an
+// order-preserving unsigned code (-0 folded into +0 first, as fp compare
+// treats them equal), above the inverted index. 0 is "no candidate" (below
+// the code of every real score, -inf included).
+__device__ __forceinline__ uint64_t pack_key(float x, int idx) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t k) {
+  return (int)(0xffffffffu - (uint32_t)k);
+}
+
+// One DPP step of a wave maximum: combine with the lane the control selects.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes of a wave (uniform result). Within each row of 16
+// lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and
+// row_mirror leave every lane with its row's maximum; the four rows are then
+// combined through readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max<0xb1>(v);
+  v = dpp_max<0x4e>(v);
+  v = dpp_max<0x141>(v);
+  v = dpp_max<0x140>(v);
+  uint64_t m = readlane_u64(v, 0);
+  const uint64_t m1 = readlane_u64(v, 16), m2 = readlane_u64(v, 32), m3 = readlane_u64(v, 48);
+  m = m1 > m ? m1 : m;
+  m = m2 > m ? m2 : m;
+  m = m3 > m ? m3 : m;
+  return m;
+}
+
+// The w_keep best keys (unique, 0 = none) held by a wave's lanes, C per lane:
+// w_keep rounds of a wave maximum, each round over the keys below the
+// previous round's winner. out[r] receives rank r (0 where there is none).
+// Call with every lane of the wave; out is written by lane 0.
+template <int C>
+__device__ __forceinline__ void wave_topw(const uint64_t (&k)[C], int w_keep, uint64_t* out) {
+  uint64_t prev = ~(uint64_t)0;
+  for (int r = 0; r < w_keep; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) best = (k[c] < prev && k[c] > best) ? k[c] : best;
+    best = wave_max_u64(best);
+    if ((threadIdx.x & 63) == 0) out[r] = best;
+    prev = best;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // workgroup top-W of register-held (key, index) candidates
 // ---------------------------------------------------------------------------
@@ -470,16 +537,15 @@ __device__ void hyp_insert(HypSmem<WMAX>& h, int W, float norm, float raw, int l
 template <int WMAX>
 __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
   constexpr int kStage = 4 * kThreads;  // tile partials staged per pass
-  __shared__ SelSmem<WMAX> sm;
   __shared__ HypSmem<WMAX> hy;
   __shared__ float lse[WMAX];
   __shared__ float srow[WMAX];
   __shared__ float stage_m[kStage], stage_s[kStage];
   __shared__ float lse_m[WMAX], lse_s[WMAX];
-  __shared__ int nslot_par[WMAX], nslot_tok[WMAX], nslot_rank[WMAX];
-  __shared__ float nslot_s[WMAX];
+  __shared__ uint64_t wave_best[kWaves][WMAX];
+  __shared__ uint64_t final_best[WMAX];
   __shared__ int plan[kPlanStride];
-  __shared__ int live_sh, done_sh;
+  __shared__ int done_sh;
   __shared__ double lp_t, lp_T;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int W = a.W, V = a.V, t = a.t;
@@ -526,7 +592,6 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
     lp_t = st.lpt[t];
     lp_T = st.lpt[a.T];
   }
-  sel_init(sm);
   __syncthreads();
 
   if (done_sh) {  // finished items: no-op outputs
@@ -588,10 +653,10 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
                                                                    : -kInf;
   __syncthreads();
 
-  // score + prune: top-W over the listed candidates, in batches, carrying the
-  // running top-W from one batch to the next
-  float carry_x = -kInf;
-  int carry_i = 0x7fffffff;
+  // score + prune: each wave keeps the top-W of its lanes' candidates, batch by
+  // batch (the running top-W rides along as one more candidate of lanes < W);
+  // then wave 0 merges the waves' lists
+  uint64_t carry = 0;
   for (int base = 0; base < n_entries; base += kThreads * kMergeNE) {
     if (base > 0) {
 #pragma unroll
@@ -601,146 +666,143 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
         lv[q] = e < n_entries ? pv[e] : 0;
       }
     }
-    float x[kMergeNE + 1];
-    int id[kMergeNE + 1];
-    float gm = carry_x;
+    uint64_t key[kMergeNE + 1];
 #pragma unroll
     for (int q = 0; q < kMergeNE; ++q) {
       const int e = base + q * kThreads + tid;
-      const int w = e / per_row;
-      x[q] = -kInf;
-      id[q] = 0x7fffffff;
+      key[q] = 0;
       if (e < n_entries) {
+        const int w = e / per_row;
         const float lw = lse[w];
         if (lx[q] > -kInf && lw > -kInf) {
           const float logp = lx[q] - lw;   // fp32 log-probability
-          x[q] = srow[w] + logp;           // fp32 candidate score
-          id[q] = w * V + lv[q];
+          const float c = srow[w] + logp;  // fp32 candidate score
+          if (c > -kInf) key[q] = pack_key(c, w * V + lv[q]);
         }
       }
-      gm = fmaxf(gm, x[q]);
     }
-    x[kMergeNE] = carry_x;
-    id[kMergeNE] = carry_i;
-    __syncthreads();  // the carry was read from sm.ox before sm is reused
-    sel_init(sm);
-    group_maxima(gm, sm.gmax, sm.wmax);
-    __syncthreads();
-    group_tau(sm, W);
-    select_from_tau<WMAX, kMergeNE + 1>(x, [&](int i) { return id[i]; }, W, sm);
-    if (tid < W) {
-      carry_x = sm.ox[tid];
-      carry_i = sm.oi[tid];
-    } else {
-      carry_x = -kInf;
-      carry_i = 0x7fffffff;
-    }
-  }
-
-  // finalize (one thread, on LDS; W <= 16 selections)
-  if (tid == 0) {
-    int live = 0;
-    float best_raw = -kInf;
-    for (int k = 0; k < W; ++k) {
-      const float c = sm.ox[k];
-      const int j = sm.oi[k];
-      if (!(c > -kInf)) continue;
-      if (best_raw == -kInf) best_raw = c;
-      const int p = j / V;
-      const int tok = j - p * V;
-      if (a.eos >= 0 && tok == a.eos) {
-        const float norm = (float)((double)c / lp_t);
-        hyp_insert(hy, W, norm, c, t, t, k, p, tok);
-      } else {
-        nslot_par[live] = p;
-        nslot_tok[live] = tok;
-        nslot_rank[live] = k;
-        nslot_s[live] = c;
-        ++live;
-      }
-    }
-    int d = 0;
-    if (live == 0) {
-      d = 1;
-    } else if (hy.count == W) {
-      float worst = kInf;
-      for (int i = 0; i < W; ++i) worst = fminf(worst, hy.norm[i]);
-      if (a.stop == BS_STOP_TRUE) {
-        d = 1;
-      } else if (a.stop == BS_STOP_HEURISTIC) {
-        d = worst >= (float)((double)best_raw / lp_t);
-      } else {
-        const float best_live = nslot_s[0];
-        const double lp = (a.alpha > 0.0 && best_live <= 0.0f) ? lp_T : lp_t;
-        d = worst >= (float)((double)best_live / lp);
-      }
-    }
-    live_sh = live;
-    st.done[b] = (uint8_t)d;
-    a.out_done[b] = (uint8_t)d;
-
-    // reorder plan: distinct parents of the slots that moved, each with the
-    // list of slots it is copied to (grouped by parent)
-    int nsrc = 0, ndst = 0;
-    if (!d) {
-      for (int i = 0; i < live; ++i) {
-        const int p = nslot_par[i];
-        if (p == i) continue;
-        bool seen = false;
-        for (int q = 0; q < nsrc; ++q) seen |= (plan[2 + q] == p);
-        if (!seen) plan[2 + nsrc++] = p;
-      }
-      for (int q = 0; q < nsrc; ++q) {
-        int cnt = 0;
-        for (int i = 0; i < live; ++i) {
-          if (nslot_par[i] != i && nslot_par[i] == plan[2 + q]) {
-            plan[2 + 2 * kMaxBeam + ndst++] = i;
-            ++cnt;
-          }
-        }
-        plan[2 + kMaxBeam + q] = cnt;
-      }
-    }
-    plan[0] = nsrc;
-    plan[1] = ndst;
+    key[kMergeNE] = carry;
+    wave_topw<kMergeNE + 1>(key, W, wave_best[wave]);
+    carry = lane < W ? wave_best[wave][lane] : 0;
   }
   __syncthreads();
 
-  // write back: plan, finished set, selection, compacted slots (live ones in
-  // rank order, then dead ones), backpointers
-  if (tid < 2 + 3 * kMaxBeam) st.plan[b * kPlanStride + tid] = plan[tid];
-  if (tid < W) {
-    const int e = b * W + tid;
-    st.hnorm[e] = hy.norm[tid];
-    st.hraw[e] = hy.raw[tid];
-    st.hlen[e] = hy.len[tid];
-    st.hstep[e] = hy.step[tid];
-    st.hrank[e] = hy.rank[tid];
-    st.hpar[e] = hy.par[tid];
-    st.htok[e] = hy.tok[tid];
-    const float c = sm.ox[tid];
-    st.sel_j[e] = (c > -kInf) ? sm.oi[tid] : -1;
-    st.sel_c[e] = c;
-    const int i = tid;
-    if (i < live_sh) {
-      st.s[e] = nslot_s[i];
-      st.slot_rank[e] = nslot_rank[i];
-      a.out_beam[e] = nslot_par[i];
-      a.out_tok[e] = nslot_tok[i];
-      a.out_score[e] = nslot_s[i];
-      st.bp_par[bpbase + i] = nslot_par[i];
-      st.bp_tok[bpbase + i] = nslot_tok[i];
+  if (wave != 0) return;
+
+  // --- wave 0: final top-W, then the finalize sub-step with lane k holding
+  // the rank-k selection
+  {
+    uint64_t k4[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) k4[w] = lane < W ? wave_best[w][lane] : 0;
+    wave_topw<kWaves>(k4, W, final_best);
+  }
+  const uint64_t key = lane < W ? final_best[lane] : 0;
+  const bool valid = key != 0;
+  const float c = key_score(key);
+  const int j = key_index(key);
+  const int p = valid ? j / V : lane;
+  const int tok = valid ? j - p * V : a.pad;
+  const bool is_eos = valid && a.eos >= 0 && tok == a.eos;
+  const bool is_live = valid && !is_eos;
+  const uint64_t lt = (lane == 0) ? 0 : (~(uint64_t)0 >> (64 - lane));  // lanes below
+  const uint64_t live_mask = __ballot(is_live);
+  const uint64_t eos_mask = __ballot(is_eos);
+  const int slot = __popcll(live_mask & lt);  // compacted slot of a live selection
+  const int nlive = __popcll(live_mask);
+
+  // EOS selections enter the finished set in rank order
+  const float norm = (float)((double)c / lp_t);
+  for (uint64_t m = eos_mask; m; m &= m - 1) {
+    const int e = __builtin_ctzll(m);
+    const float ne = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(norm), e));
+    const float ce = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e));
+    const int pe = __builtin_amdgcn_readlane(p, e);
+    if (lane == 0) hyp_insert(hy, W, ne, ce, t, t, e, pe, a.eos);
+  }
+
+  // stop rule
+  int d = 0;
+  if (nlive == 0) {
+    d = 1;
+  } else if (hy.count == W) {
+    float worst = kInf;
+    for (int i = 0; i < W; ++i) worst = fminf(worst, hy.norm[i]);
+    const float best_raw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 0));
+    if (a.stop == BS_STOP_TRUE) {
+      d = 1;
+    } else if (a.stop == BS_STOP_HEURISTIC) {
+      d = worst >= (float)((double)best_raw / lp_t);
     } else {
-      st.s[e] = -kInf;
-      st.slot_rank[e] = W;
-      a.out_beam[e] = i;
-      a.out_tok[e] = a.pad;
-      a.out_score[e] = -kInf;
-      st.bp_par[bpbase + i] = i;
-      st.bp_tok[bpbase + i] = a.pad;
+      const int first = __builtin_ctzll(live_mask);
+      const float best_live = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), first));
+      const double lp = (a.alpha > 0.0 && best_live <= 0.0f) ? lp_T : lp_t;
+      d = worst >= (float)((double)best_live / lp);
     }
   }
-  if (tid == 0) st.hcount[b] = hy.count;
+
+  // reorder plan: the distinct parents of moved slots (in parent order), each
+  // with the slots it is copied to (in slot order)
+  const bool moved = is_live && p != slot && !d;
+  int nsrc = 0, ndst = 0;
+  for (int q = 0; q < W; ++q) {
+    uint64_t m = __ballot(moved && p == q);
+    if (!m) continue;
+    if (lane == 0) plan[2 + nsrc] = q;
+    int cnt = 0;
+    for (; m; m &= m - 1) {
+      const int l = __builtin_ctzll(m);
+      const int sl = __builtin_amdgcn_readlane(slot, l);
+      if (lane == 0) plan[2 + 2 * kMaxBeam + ndst] = sl;
+      ++ndst;
+      ++cnt;
+    }
+    if (lane == 0) plan[2 + kMaxBeam + nsrc] = cnt;
+    ++nsrc;
+  }
+  if (lane == 0) {
+    plan[0] = nsrc;
+    plan[1] = ndst;
+    st.done[b] = (uint8_t)d;
+    a.out_done[b] = (uint8_t)d;
+    st.hcount[b] = hy.count;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // write back: plan, finished set, selection, slots, backpointers
+  if (lane < 2 + 3 * kMaxBeam) st.plan[b * kPlanStride + lane] = plan[lane];
+  if (lane < W) {
+    const int e = b * W + lane;
+    st.hnorm[e] = hy.norm[lane];
+    st.hraw[e] = hy.raw[lane];
+    st.hlen[e] = hy.len[lane];
+    st.hstep[e] = hy.step[lane];
+    st.hrank[e] = hy.rank[lane];
+    st.hpar[e] = hy.par[lane];
+    st.htok[e] = hy.tok[lane];
+    st.sel_j[e] = valid ? j : -1;
+    st.sel_c[e] = valid ? c : -kInf;
+    if (is_live) {  // rank `lane` becomes slot `slot`
+      const int r = b * W + slot;
+      st.s[r] = c;
+      st.slot_rank[r] = lane;
+      a.out_beam[r] = p;
+      a.out_tok[r] = tok;
+      a.out_score[r] = c;
+      st.bp_par[bpbase + slot] = p;
+      st.bp_tok[bpbase + slot] = tok;
+    }
+    if (lane >= nlive) {  // dead slot `lane`
+      st.s[e] = -kInf;
+      st.slot_rank[e] = W;
+      a.out_beam[e] = lane;
+      a.out_tok[e] = a.pad;
+      a.out_score[e] = -kInf;
+      st.bp_par[bpbase + lane] = lane;
+      st.bp_tok[bpbase + lane] = a.pad;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
