@@ -87,12 +87,6 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 // wave reductions
 // ---------------------------------------------------------------------------
 
-// Butterfly sum over the wave (every lane gets the same, reproducible value).
-__device__ __forceinline__ float wave_sum(float s) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  return s;
-}
 
 // Candidate keys packed into one unsigned 64-bit word so that a plain unsigned
 // maximum picks (score desc, index asc): the score's bits, mapped to an
@@ -144,6 +138,55 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
+// Float maximum and sum over a wave with the same DPP row steps, the four
+// row results combined through readlane in a fixed order (uniform result;
+// the sum is reproducible).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));
+  v = fmaxf(v, dpp_f<0x4e>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v = v + dpp_f<0xb1>(v);
+  v = v + dpp_f<0x4e>(v);
+  v = v + dpp_f<0x141>(v);
+  v = v + dpp_f<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Step 1 of the selection. m is this thread's largest key. The workgroup's
+// threads form kGroups groups of 16 lanes; each group's maximum goes to
+// sm.gmax and each wave's maximum to sm.wmax. Returns the wave maximum.
+__device__ __forceinline__ float group_maxima(float m, float* gmax, float* wmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  m = fmaxf(m, dpp_f<0xb1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_f<0x4e>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_f<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_f<0x140>(m));  // row_mirror: every lane has its row's max
+  if ((lane & 15) == 0) gmax[threadIdx.x >> 4] = m;
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
+  m = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  if (lane == 0) wmax[wave] = m;
+  return m;
+}
+
 // The w_keep best keys (unique, 0 = none) held by a wave's lanes, C per lane:
 // w_keep rounds of a wave maximum, each round over the keys below the
 // previous round's winner. out[r] receives rank r (0 where there is none).
@@ -191,20 +234,6 @@ __device__ __forceinline__ void sel_init(SelSmem<WMAX>& sm) {
     sm.ox[threadIdx.x] = -kInf;
     sm.oi[threadIdx.x] = 0x7fffffff;
   }
-}
-
-// Step 1 of the selection. m is this thread's largest key. The workgroup's
-// threads form kGroups groups of 16 lanes; each group's maximum goes to
-// sm.gmax and each wave's maximum to sm.wmax. Returns the wave maximum.
-__device__ __forceinline__ float group_maxima(float m, float* gmax, float* wmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((lane & 15) == 0) gmax[threadIdx.x >> 4] = m;
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (lane == 0) wmax[wave] = m;
-  return m;
 }
 
 // Step 2 (after a barrier): tau = the w_keep-th largest of the group maxima.
@@ -433,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
 #pragma unroll
     for (int i = 0; i < EPT; ++i) s += exp2f((x[i] - M) * kLog2e);
   }
-  s = wave_sum(s);
+  s = wave_sum_f(s);
   if (lane == 0) sm.wsum[wave] = s;
 
   // prune, stage 1: the tile's best W raw logits (monotone in log-prob)
@@ -631,15 +660,14 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
       const int lo = max(base, w * a.tiles), hi = min(base + kStage, (w + 1) * a.tiles);
       float m = -kInf;
       for (int e = lo + lane; e < hi; e += 64) m = fmaxf(m, stage_m[e - base]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      m = wave_max_f(m);
       float sum = 0.0f;
       if (m > -kInf)
         for (int e = lo + lane; e < hi; e += 64) {
           const float mt = stage_m[e - base];
           if (mt > -kInf) sum += stage_s[e - base] * exp2f((mt - m) * kLog2e);
         }
-      sum = wave_sum(sum);
+      sum = wave_sum_f(sum);
       if (lane == 0) {  // combine with the previous pass (tiles beyond kStage)
         float pm = lse_m[w], ps = lse_s[w];
         lse_combine(pm, ps, m, sum);
