@@ -168,25 +168,6 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// Step 1 of the selection. m is this thread's largest key. The workgroup's
-// threads form kGroups groups of 16 lanes; each group's maximum goes to
-// sm.gmax and each wave's maximum to sm.wmax. Returns the wave maximum.
-__device__ __forceinline__ float group_maxima(float m, float* gmax, float* wmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  m = fmaxf(m, dpp_f<0xb1>(m));   // quad_perm [1,0,3,2]
-  m = fmaxf(m, dpp_f<0x4e>(m));   // quad_perm [2,3,0,1]
-  m = fmaxf(m, dpp_f<0x141>(m));  // row_half_mirror
-  m = fmaxf(m, dpp_f<0x140>(m));  // row_mirror: every lane has its row's max
-  if ((lane & 15) == 0) gmax[threadIdx.x >> 4] = m;
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
-  m = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-  if (lane == 0) wmax[wave] = m;
-  return m;
-}
-
 // The w_keep best keys (unique, 0 = none) held by a wave's lanes, C per lane:
 // w_keep rounds of a wave maximum, each round over the keys below the
 // previous round's winner. out[r] receives rank r (0 where there is none).
@@ -202,152 +183,6 @@ __device__ __forceinline__ void wave_topw(const uint64_t (&k)[C], int w_keep, ui
     if ((threadIdx.x & 63) == 0) out[r] = best;
     prev = best;
   }
-}
-
-// ---------------------------------------------------------------------------
-// workgroup top-W of register-held (key, index) candidates
-// ---------------------------------------------------------------------------
-
-template <int WMAX>
-struct SelSmem {
-  float gmax[kGroups];
-  float wmax[kWaves];
-  float wsum[kWaves];
-  float rx[kWaves];
-  int ri[kWaves];
-  float tau;
-  int count;
-  float ox[WMAX];
-  int oi[WMAX];
-  alignas(16) float lx[kListCap];
-  alignas(16) int li[kListCap];
-};
-
-// Resets the selection scratch; a barrier must follow before it is used.
-template <int WMAX>
-__device__ __forceinline__ void sel_init(SelSmem<WMAX>& sm) {
-  if (threadIdx.x == 0) {
-    sm.count = 0;
-    sm.tau = -kInf;
-  }
-  if (threadIdx.x < WMAX) {
-    sm.ox[threadIdx.x] = -kInf;
-    sm.oi[threadIdx.x] = 0x7fffffff;
-  }
-}
-
-// Step 2 (after a barrier): tau = the w_keep-th largest of the group maxima.
-// The group maxima are distinct elements, so at least w_keep elements are
-// >= tau: it is a lower bound on the w_keep-th best key. When fewer than
-// w_keep groups hold a finite key, tau is -inf. Ends with a barrier.
-template <int WMAX>
-__device__ __forceinline__ void group_tau(SelSmem<WMAX>& sm, int w_keep) {
-  const int g = threadIdx.x;
-  if (g < kGroups) {
-    const float v = sm.gmax[g];
-    int rank = 0;
-#pragma unroll
-    for (int h = 0; h < kGroups; ++h) {
-      const float u = sm.gmax[h];
-      rank += (u > v || (u == v && h < g)) ? 1 : 0;
-    }
-    if (rank == w_keep - 1) sm.tau = v;
-  }
-  __syncthreads();
-}
-
-// Step 3: the w_keep (<= WMAX) best of all candidates held by the workgroup,
-// written to sm.ox/sm.oi in rank order; ranks without a finite candidate keep
-// (-inf, INT_MAX). Keys of -inf are never candidates; indices are unique.
-// Only keys >= sm.tau are listed in LDS and ranked by counting. A list that
-// would overflow (massive ties) falls back to w_keep rounds of a workgroup
-// argmax over the registers. Ends with a barrier.
-template <int WMAX, int NE, typename IdFn>
-__device__ void select_from_tau(const float (&x)[NE], IdFn idf, int w_keep, SelSmem<WMAX>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float tau = sm.tau;
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) c += (x[i] > -kInf && x[i] >= tau) ? 1 : 0;
-  int p = c ? atomicAdd(&sm.count, c) : 0;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    if (x[i] > -kInf && x[i] >= tau) {
-      if (p < kListCap) {
-        sm.lx[p] = x[i];
-        sm.li[p] = idf(i);
-      }
-      ++p;
-    }
-  }
-  __syncthreads();
-  const int n = sm.count;
-  if (n <= kListCap) {
-    for (int e = tid; e < n; e += kThreads) {
-      const float xe = sm.lx[e];
-      const int ie = sm.li[e];
-      int rank = 0;
-      // four list entries per 16-byte LDS read
-      for (int f0 = 0; f0 < n; f0 += 4) {
-        const float4 xs = *reinterpret_cast<const float4*>(&sm.lx[f0]);
-        const int4 is = *reinterpret_cast<const int4*>(&sm.li[f0]);
-        rank += (f0 + 0 < n && better(xs.x, is.x, xe, ie)) ? 1 : 0;
-        rank += (f0 + 1 < n && better(xs.y, is.y, xe, ie)) ? 1 : 0;
-        rank += (f0 + 2 < n && better(xs.z, is.z, xe, ie)) ? 1 : 0;
-        rank += (f0 + 3 < n && better(xs.w, is.w, xe, ie)) ? 1 : 0;
-      }
-      if (rank < w_keep) {
-        sm.ox[rank] = xe;
-        sm.oi[rank] = ie;
-      }
-    }
-  } else {
-    // Repeated extraction of the best key strictly worse than the previous
-    // one. Uniform control flow: n is the same for every thread.
-    float px = kInf;
-    int pi = -1;
-    for (int r = 0; r < w_keep; ++r) {
-      float bx = -kInf;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int ii = idf(i);
-        if (x[i] > -kInf && better(px, pi, x[i], ii) && better(x[i], ii, bx, bi)) {
-          bx = x[i];
-          bi = ii;
-        }
-      }
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ox = __shfl_xor(bx, o);
-        const int oi = __shfl_xor(bi, o);
-        if (better(ox, oi, bx, bi)) {
-          bx = ox;
-          bi = oi;
-        }
-      }
-      __syncthreads();
-      if (lane == 0) {
-        sm.rx[wave] = bx;
-        sm.ri[wave] = bi;
-      }
-      __syncthreads();
-      bx = sm.rx[0];
-      bi = sm.ri[0];
-      for (int w = 1; w < kWaves; ++w)
-        if (better(sm.rx[w], sm.ri[w], bx, bi)) {
-          bx = sm.rx[w];
-          bi = sm.ri[w];
-        }
-      if (bx == -kInf) break;
-      if (tid == 0) {
-        sm.ox[r] = bx;
-        sm.oi[r] = bi;
-      }
-      px = bx;
-      pi = bi;
-    }
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -429,9 +264,43 @@ struct K1Args {
   int* pv;              // [rows][tiles][WMAX] their columns
 };
 
+// tau for a tile: the w_keep-th largest of the kGroups group maxima, which is
+// a lower bound on the tile's w_keep-th best logit (the group maxima are
+// distinct elements). Every wave computes it on its own: lane l of each
+// 16-lane row holds gmax[l % 16] and counts, over the 15 DPP row rotations,
+// how many of the others are larger (gt) and at least as large (ge). A value
+// with gt <= w-1 and ge+1 >= w is the w-th largest; all such lanes hold the
+// same value, so the rotation direction does not matter.
+template <int R>
+__device__ __forceinline__ void rank_rotations(float g, int& gt, int& ge) {
+  if constexpr (R <= 15) {
+    const float o = dpp_f<0x120 + R>(g);  // row_ror:R
+    gt += o > g ? 1 : 0;
+    ge += o >= g ? 1 : 0;
+    rank_rotations<R + 1>(g, gt, ge);
+  }
+}
+
+__device__ __forceinline__ float tile_tau(const float* gmax, int w_keep) {
+  const int lane = threadIdx.x & 63;
+  const float g = gmax[lane & 15];
+  int gt = 0, ge = 0;
+  rank_rotations<1>(g, gt, ge);
+  const uint64_t q = __ballot(lane < 16 && gt <= w_keep - 1 && ge + 1 >= w_keep);
+  const int l = __builtin_ctzll(q);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), l));
+}
+
 template <int WMAX, typename T, int EPT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
-  __shared__ SelSmem<WMAX> sm;
+  constexpr int kRegion = kListCap / kWaves;  // candidate slots of one wave
+  __shared__ float gmax[kGroups];
+  __shared__ float wm[kWaves], ws[kWaves];
+  __shared__ int wn[kWaves];
+  __shared__ float rx[kWaves];
+  __shared__ int ri[kWaves];
+  __shared__ alignas(16) float lx[kListCap];
+  __shared__ alignas(16) int li[kListCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.y, c = blockIdx.x;
   const int b = r / a.W;
@@ -441,46 +310,170 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const int v0 = c * a.tile;
   const int vend = min(a.V, v0 + a.tile);
+  const int W = a.W;
 
   float x[EPT];
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
-  sel_init(sm);
 
-  // the tile maximum M, and the 16-lane group maxima that bound the W-th best
-  float tmax = -kInf;
+  // expand, per wave: the wave maximum mw and sum of exp(x - mw); the 16-lane
+  // row maxima double as the group maxima for tau
+  float m = -kInf;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) tmax = fmaxf(tmax, x[i]);
-  group_maxima(tmax, sm.gmax, sm.wmax);
-  __syncthreads();
-  float M = sm.wmax[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wmax[w]);
-
-  // expand: sum of exp(x - M) over the tile
+  for (int i = 0; i < EPT; ++i) m = fmaxf(m, x[i]);
+  m = fmaxf(m, dpp_f<0xb1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_f<0x4e>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_f<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_f<0x140>(m));  // row_mirror: every lane has its row's max
+  if ((lane & 15) == 0) gmax[tid >> 4] = m;
+  const float mw = fmaxf(
+      fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+      fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
   float s = 0.0f;
-  if (M > -kInf) {
+  if (mw > -kInf) {
+    // exp(x - mw) = 2^(x log2e - mw log2e); terms below 2^-126 flush to zero,
+    // far below the sum's own rounding (the sum is at least 1)
+    const float off = -mw * kLog2e;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) s += exp2f((x[i] - M) * kLog2e);
+    for (int i = 0; i < EPT; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, off));
   }
   s = wave_sum_f(s);
-  if (lane == 0) sm.wsum[wave] = s;
+  if (lane == 0) {
+    wm[wave] = mw;
+    ws[wave] = s;
+  }
+  __syncthreads();
 
-  // prune, stage 1: the tile's best W raw logits (monotone in log-prob)
-  group_tau(sm, a.W);
-  select_from_tau<WMAX, EPT>(x, [&](int i) { return TileMap<T, ALIGNED>::col(v0, i); }, a.W,
-                             sm);
+  // prune, stage 1: list every logit >= tau in this wave's LDS region
+  // (ballot + mbcnt compaction, no atomics); -inf is never a candidate
+  float tau = tile_tau(gmax, W);
+  if (!(tau > -kInf)) tau = -3.402823466e38f;
+  int woff = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const bool cand = x[i] >= tau;
+    const uint64_t bm = __ballot(cand);
+    if (bm) {
+      const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                 (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0));
+      if (cand && pos < kRegion) {
+        lx[wave * kRegion + pos] = x[i];
+        li[wave * kRegion + pos] = TileMap<T, ALIGNED>::col(v0, i);
+      }
+      woff += __popcll(bm);
+    }
+  }
+  if (lane == 0) wn[wave] = woff;
+  __syncthreads();
 
   const int64_t pt = (int64_t)r * a.tiles + c;
-  if (tid == 0) {
-    float S = sm.wsum[0];
+  if (tid == 0) {  // the tile's (max, sum exp) from the four waves, in order
+    float M = wm[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) S += sm.wsum[w];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
+    float S = 0.0f;
+    if (M > -kInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (wm[w] > -kInf) S += ws[w] * exp2f((wm[w] - M) * kLog2e);
+    }
     a.pm[pt] = M;
     a.ps[pt] = S;
   }
-  if (tid < WMAX) {
-    a.px[pt * WMAX + tid] = sm.ox[tid];
-    a.pv[pt * WMAX + tid] = sm.oi[tid];
+  int n[kWaves], ntot = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    n[w] = wn[w];
+    overflow |= n[w] > kRegion;
+    ntot += n[w];
+  }
+  float* ox = a.px + pt * WMAX;
+  int* oi = a.pv + pt * WMAX;
+  if (tid < WMAX && tid >= min(ntot, W)) {  // ranks without a candidate
+    ox[tid] = -kInf;
+    oi[tid] = 0x7fffffff;
+  }
+  if (!overflow) {
+    // rank every listed candidate by counting the better ones, one candidate
+    // per thread over the concatenated regions; the ranks below W go straight
+    // to the tile's output
+    int pre[kWaves];
+    pre[0] = 0;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) pre[w] = pre[w - 1] + n[w - 1];
+    for (int e = tid; e < ntot; e += kThreads) {
+      int w = 0;
+#pragma unroll
+      for (int u = 1; u < kWaves; ++u) w = e >= pre[u] ? u : w;
+      const float xe = lx[w * kRegion + e - pre[w]];
+      const int ie = li[w * kRegion + e - pre[w]];
+      int rank = 0;
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u) {
+        const float* bx = lx + u * kRegion;
+        const int* bi = li + u * kRegion;
+        for (int f0 = 0; f0 < n[u]; f0 += 4) {
+          const float4 xs = *reinterpret_cast<const float4*>(bx + f0);
+          const int4 is = *reinterpret_cast<const int4*>(bi + f0);
+          rank += (f0 + 0 < n[u] && better(xs.x, is.x, xe, ie)) ? 1 : 0;
+          rank += (f0 + 1 < n[u] && better(xs.y, is.y, xe, ie)) ? 1 : 0;
+          rank += (f0 + 2 < n[u] && better(xs.z, is.z, xe, ie)) ? 1 : 0;
+          rank += (f0 + 3 < n[u] && better(xs.w, is.w, xe, ie)) ? 1 : 0;
+        }
+      }
+      if (rank < W) {
+        ox[rank] = xe;
+        oi[rank] = ie;
+      }
+    }
+    return;
+  }
+  // A wave listed more candidates than its region holds (massive ties):
+  // W rounds of a workgroup argmax over the registers, each round taking the
+  // best key strictly worse than the previous one. Uniform control flow.
+  float px = kInf;
+  int pi = -1;
+  for (int rk = 0; rk < W; ++rk) {
+    float bx = -kInf;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int ii = TileMap<T, ALIGNED>::col(v0, i);
+      if (x[i] > -kInf && better(px, pi, x[i], ii) && better(x[i], ii, bx, bi)) {
+        bx = x[i];
+        bi = ii;
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float oxv = __shfl_xor(bx, o);
+      const int oiv = __shfl_xor(bi, o);
+      if (better(oxv, oiv, bx, bi)) {
+        bx = oxv;
+        bi = oiv;
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      rx[wave] = bx;
+      ri[wave] = bi;
+    }
+    __syncthreads();
+    bx = rx[0];
+    bi = ri[0];
+    for (int w = 1; w < kWaves; ++w)
+      if (better(rx[w], ri[w], bx, bi)) {
+        bx = rx[w];
+        bi = ri[w];
+      }
+    if (bx == -kInf) break;
+    if (tid == 0) {
+      ox[rk] = bx;
+      oi[rk] = bi;
+    }
+    px = bx;
+    pi = bi;
   }
 }
 

@@ -1,25 +1,28 @@
 """Benchmark: beam steps per second and achieved HBM bandwidth on one MI355X.
 
-Workload: the Llama-3-8B-shaped batched beam search -- B=8 items, W=4 beams,
-V=128256 bf16 logits (N(0,3) + Zipf(1.0) token bias), EOS = V-1 under the
-Zipf term, HF-style length penalty |y|^1.0 with early stopping "true", 200
-decode steps per search, KV cache 32 layers x 8 KV heads x 128 dims bf16
-(128 KiB per token per beam) behind a 1000-token prompt that is shared and
-never moved.
+Default workload (the headline line): the Llama-3-8B-shaped batched beam
+search -- B=8 items, W=4 beams, V=128256 bf16 logits (N(0,3) + Zipf(1.0)
+token bias), EOS = V-1 under the Zipf term, HF-style length penalty |y|^1.0
+with early stopping "true", 200 decode steps per search, KV cache 32 layers x
+8 KV heads x 128 dims bf16 (128 KiB per token per beam) behind a 1000-token
+prompt that is shared and never moved.
 
 One benchmark step is one decode step t of the search: bs_step (expand,
-score, prune, finalize over the [32, 128256] logits) followed by
-bs_reorder_kv with gen_len = t over the 64 (layer, K|V) planes. Steps cycle
-through t = 1..200; a new search starts (bs_reset) every 200 steps. Logits
-come from a pool of 64 device buffers (525 MB, larger than the 256 MB
-Infinity Cache) filled with 16 distinct seeded steps.
+score, prune, finalize over the [B*W, V] logits) followed by bs_reorder_kv
+with gen_len = t over the (layer, K|V) planes. Steps cycle through
+t = 1..max_steps; a new search starts (bs_reset) after max_steps steps.
+Logits come from a pool of device buffers larger than the 256 MB Infinity
+Cache, filled with distinct seeded steps.
 
-Output: one JSON line. ``value`` is beam steps/s over the timed steps with all
+``--workload tbase`` and ``--workload wide`` run the Transformer-base and
+wide-beam searches the same way; ``--workload verify`` times bs_verify on the
+blockwise-parallel verify shape (B=64, k=8, V=32000 fp32).
+
+Output: one JSON line. ``value`` is steps/s over the timed steps with all
 inputs resident in HBM. ``roofline`` is for the dominant kernel (the KV
-reorder): algorithmic bytes (distinct parents read once + moved slots written,
-over gen_len positions and 64 planes) over its launch durations measured with
-HIP events on the library's stream. ``cpu_baseline`` times the CPU oracle on
-a bounded sample of the same workload.
+reorder; for verify, the verify call): algorithmic bytes over launch
+durations measured with HIP events on the library's stream. ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,6 +38,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "beam steps/sec and achieved HBM GB/s (% of peak) at B,W,V; 1 GPU"
+
+# per workload: logit pool buffers and how many distinct generated steps fill it
+POOLS = {"llama3_8b": (64, 16), "tbase": (64, 16), "wide": (3, 3)}
 
 
 def parse():
@@ -42,8 +49,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--pool", type=int, default=64)
-    ap.add_argument("--distinct", type=int, default=16)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "tbase", "wide", "verify"])
+    ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
+    ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8)
     ap.add_argument("--events", type=int, default=1,
@@ -63,26 +72,43 @@ def main():
 
     import torch
     import beam_search_step_amd as bs
-    import synth
 
     bs.library()  # fail loudly if the HIP library is not built
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    wl = synth.WORKLOADS["llama3_8b"]
+    if args.workload == "verify":
+        out = bench_verify(args, torch, bs, dev)
+    else:
+        out = bench_search(args, torch, bs, dev)
+    if args.copy_reference:
+        out["copy_reference"] = copy_reference(torch, dev)
+    print(json.dumps(out))
+
+
+def bench_search(args, torch, bs, dev):
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
     B, W, V, T = wl.batch, wl.beam, wl.vocab, wl.max_steps
     planes_n = 2 * wl.layers
-    bpp = wl.kv_bytes_per_pos                      # 2048 B per position per plane
-    assert W * V == 513024 and wl.kv_bytes_per_token == 131072
+    bpp = wl.kv_bytes_per_pos
+    if wl.name == "llama3_8b":
+        assert W * V == 513024 and wl.kv_bytes_per_token == 131072
+    pool_n, distinct_n = POOLS[wl.name]
+    pool_n = args.pool or pool_n
+    distinct_n = min(args.distinct or distinct_n, pool_n)
 
     # ---- inputs resident in HBM ------------------------------------------------
     t0 = time.time()
-    distinct = [synth.logits(wl, s + 1) for s in range(args.distinct)]
+    ldt = torch.int16 if wl.dtype == "bf16" else torch.float32
+    pool = torch.empty((pool_n, wl.rows, V), dtype=ldt, device=dev)
+    for s in range(distinct_n):
+        lg = synth.logits(wl, s + 1)
+        src = torch.from_numpy(lg.view(np.int16) if wl.dtype == "bf16" else lg)
+        for i in range(s, pool_n, distinct_n):
+            pool[i].copy_(src)
     gen_s = time.time() - t0
-    pool = torch.empty((args.pool, wl.rows, V), dtype=torch.int16, device=dev)
-    for i in range(args.pool):
-        pool[i].copy_(torch.from_numpy(distinct[i % args.distinct].view(np.int16)))
-    del distinct
-    kv = [torch.zeros((wl.rows, T, bpp // 2), dtype=torch.int16, device=dev)
+    kv = [torch.zeros((wl.rows, T, bpp // 4), dtype=torch.int32, device=dev)
           for _ in range(planes_n)]
     desc = bs.make_kv_desc(kv, pos_offset=0)
 
@@ -107,7 +133,7 @@ def main():
             if t == 1 and g.steps:
                 g.reset()
             o = hist[i] if record else hist[0]
-            bs.bs_step(g.h, pool[i % args.pool], *o)
+            bs.bs_step(g.h, pool[i % pool_n], *o)
             if record and args.events:
                 events[i][0].record(stream)
             bs.bs_reorder_kv(g.h, desc, t)
@@ -138,7 +164,7 @@ def main():
             prev_live = np.zeros((B, W), bool)
             prev_live[:, 0] = True
         live_rows = int(prev_live.sum())                  # rows the step had to read
-        logit_bytes.append(live_rows * V * 2 + 20 * B * W)
+        logit_bytes.append(live_rows * V * wl.elem_bytes + 20 * B * W)
         moved_total = 0
         for b in range(B):
             if dn[i, b]:
@@ -153,7 +179,7 @@ def main():
     logit_bytes = np.array(logit_bytes, np.float64)
 
     out = {
-        "metric": "beam steps/sec and achieved HBM GB/s (% of peak) at B,W,V; 1 GPU",
+        "metric": METRIC,
         "value": args.steps / elapsed,
         "unit": "beam steps/s",
         "n_gpus": 1,
@@ -166,13 +192,15 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "llama3_8b_beam_step: B=8 W=4 V=128256 bf16 logits, KV 32x8x128 bf16, "
-                        "200 steps/search, gen_len = t",
-            "batch": B, "beam": W, "vocab": V, "logits_dtype": "bf16",
+            "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
+                        f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
+                        f"gen_len = t",
+            "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype,
             "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
-            "logit_pool_buffers": args.pool,
+            "logit_pool_buffers": pool_n,
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
+        "live_item_steps": int((~dn).sum()),
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if args.events:
@@ -184,7 +212,7 @@ def main():
         out["roofline"] = {
             "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-            "traffic": measured_traffic(kv_bytes.mean()),
+            "traffic": measured_traffic(wl.name),
             "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
         }
         out["step_kernels"] = {
@@ -192,13 +220,78 @@ def main():
             "avg_us": 1e6 * d_step.mean(),
             "alg_gbs": logit_bytes[1:].sum() / d_step.sum() / 1e9,
         }
-    if args.copy_reference:
-        out["copy_reference"] = copy_reference(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n)
     out["input_generation_s"] = gen_s
     g.close()
-    print(json.dumps(out))
+    return out
+
+
+def bench_verify(args, torch, bs, dev):
+    """Blockwise-parallel verify: one step is one bs_verify call on [64, 8, 32000]
+    fp32 logits (65.5 MB) from a pool of 8 distinct buffers."""
+    import synth
+
+    cfg = synth.VERIFY
+    Bv, k, V = cfg["batch"], cfg["k"], cfg["vocab"]
+    pool_n = args.pool or cfg["pool"]
+    lgs, props = [], []
+    t0 = time.time()
+    for call in range(pool_n):
+        lg, pr = synth.verify_inputs(Bv, k, V, cfg["seed"], sigma=cfg["sigma"],
+                                     accept_p=cfg["accept_p"], plant=cfg["plant"], call=call)
+        lgs.append(torch.from_numpy(lg).to(dev))
+        props.append(torch.from_numpy(pr).to(dev))
+    gen_s = time.time() - t0
+    ver = bs.Verifier(Bv, k, V)
+    stream = torch.cuda.current_stream()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps if args.events else 0)]
+    for i in range(args.warmup):
+        ver(lgs[i % pool_n], props[i % pool_n])
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        if args.events:
+            events[i][0].record(stream)
+        ver(lgs[i % pool_n], props[i % pool_n])
+        if args.events:
+            events[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    alg = Bv * k * V * 4 + Bv * k * 4 * 2 + Bv * 4
+    out = {
+        "metric": "blockwise verify calls/sec and achieved HBM GB/s (% of peak); 1 GPU",
+        "value": args.steps / elapsed, "unit": "verify calls/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"blockwise_verify: B={Bv} k={k} V={V} fp32 logits",
+                   "batch": Bv, "k": k, "vocab": V, "logit_pool_buffers": pool_n},
+    }
+    if args.events:
+        d = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
+        ach = alg / d.mean() / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": "k4_argmax_tiles + k4_accept",
+                           "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                           "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
+    if not args.no_cpu_baseline:
+        import oracle
+        lg0 = lgs[0].cpu().numpy()
+        pr0 = props[0].cpu().numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.verify(lg0, pr0)
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / dt, "unit": "verify calls/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} oracle verify calls on one "
+                               f"buffer; host nproc={os.cpu_count()}", "seconds": dt}
+    out["input_generation_s"] = gen_s
+    ver.close()
+    return out
 
 
 def copy_reference(torch, dev):
@@ -219,9 +312,6 @@ def copy_reference(torch, dev):
     return {"bytes_read_plus_written": 2 * n, "avg_us": us, "GBs": 2 * n / us / 1e3}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_kv_reorder_llama3_8b_traffic.json")
-
-
 def k3_source_hash():
     """Hash of the KV-reorder kernel's source: counter readings are only used
     while the kernel they were taken on is unchanged."""
@@ -232,12 +322,13 @@ def k3_source_hash():
     return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
 
 
-def measured_traffic(alg_bytes_per_launch):
+def measured_traffic(workload):
     """HBM bytes per KV-reorder launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
-    None when there is none for the current kernel source."""
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy's reading), or None when there is none for the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"k3_kv_reorder_{workload}_traffic.json")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -248,9 +339,9 @@ def measured_traffic(alg_bytes_per_launch):
 
 def cpu_baseline(wl, n_steps, bpp, planes_n):
     """The CPU oracle, single-threaded on one core, on a bounded sample: the
-    first n_steps decode steps of the same search (select + apply over all 8
-    items), each followed by the oracle's KV gather over 64 planes at
-    gen_len 100 (the mean gen_len of a 200-step search)."""
+    first n_steps decode steps of the same search (select + apply over all
+    items), each followed by the oracle's KV gather over every plane at
+    gen_len = max_steps / 2 (the mean gen_len of a full search)."""
     import oracle
     import synth
 
@@ -259,7 +350,7 @@ def cpu_baseline(wl, n_steps, bpp, planes_n):
     except (AttributeError, OSError):
         pass
     ref = oracle.Search.for_workload(wl)
-    gen = 100
+    gen = wl.max_steps // 2
     host = [np.zeros((wl.rows, gen, bpp), np.uint8) for _ in range(planes_n)]
     lgs = [synth.logits(wl, t) for t in range(1, n_steps + 1)]
     t0 = time.perf_counter()
@@ -268,9 +359,9 @@ def cpu_baseline(wl, n_steps, bpp, planes_n):
         oracle.kv_reorder(host, bi, dn, gen)
     dt = time.perf_counter() - t0
     return {"value": n_steps / dt, "unit": "beam steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle steps 1-{n_steps} of the B=8 W=4 V=128256 search (select + "
-                      f"apply on all items), each with the KV gather of 64 planes at "
-                      f"gen_len {gen}; host nproc={os.cpu_count()}",
+            "sample": f"oracle steps 1-{n_steps} of the B={wl.batch} W={wl.beam} V={wl.vocab} "
+                      f"search (select + apply on all items), each with the KV gather of "
+                      f"{planes_n} planes at gen_len {gen}; host nproc={os.cpu_count()}",
             "seconds": dt}
 
 
