@@ -40,8 +40,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "beam steps/sec and achieved HBM GB/s (% of peak) at B,W,V; 1 GPU"
 
-# per workload: logit pool buffers and how many distinct generated steps fill it
-POOLS = {"llama3_8b": (64, 16), "tbase": (64, 16), "wide": (3, 3)}
+# per workload: logit pool buffers and how many distinct generated steps fill
+# them; step t reads buffer (t - 1) mod pool. The Transformer-base logits
+# change with the step (the EOS bias ramps over the first 100 steps), so its
+# pool holds every step of a search.
+POOLS = {"llama3_8b": (64, 16), "tbase": (128, 128), "wide": (3, 3)}
 
 
 def parse():
@@ -133,7 +136,7 @@ def bench_search(args, torch, bs, dev):
             if t == 1 and g.steps:
                 g.reset()
             o = hist[i] if record else hist[0]
-            bs.bs_step(g.h, pool[i % pool_n], *o)
+            bs.bs_step(g.h, pool[(t - 1) % pool_n], *o)
             if record and args.events:
                 events[i][0].record(stream)
             bs.bs_reorder_kv(g.h, desc, t)
