@@ -75,11 +75,12 @@ def library() -> ctypes.CDLL:
         L.bs_destroy.restype = None
         L.bs_verify_create.argtypes = [i32, i32, i32, i32, P, ctypes.POINTER(P)]
         L.bs_verify.argtypes = [P, P, i64, P, P, P]
+        L.bs_verify_ex.argtypes = [P, P, i64, P, i32, i32, P, P, P]
         L.bs_verify_destroy.argtypes = [P]
         L.bs_verify_destroy.restype = None
         for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_finalize",
                      "bs_last_selection", "bs_get_finished", "bs_steps_taken",
-                     "bs_verify_create", "bs_verify"):
+                     "bs_verify_create", "bs_verify", "bs_verify_ex"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -179,10 +180,28 @@ def bs_verify_create(batch: int, k: int, vocab: int, dtype: int, stream=None) ->
     return h.value
 
 
+def _verify_stride(logits) -> int:
+    """Row stride in elements of logits [B*k, S] or [B, k, S] (rows evenly spaced)."""
+    if logits.stride(-1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    if logits.dim() == 3:
+        if logits.shape[0] > 1 and logits.stride(0) != logits.shape[1] * logits.stride(1):
+            raise ValueError("rows of logits [B, k, S] must be evenly spaced")
+        return logits.stride(1)
+    return logits.stride(0)
+
+
 def bs_verify(h: int, logits, proposals, accept_len, argmax) -> None:
-    stride = logits.shape[-1] if logits.dim() == 3 else logits.stride(0)
-    _check(library().bs_verify(h, _ptr(logits), stride, _ptr(proposals), _ptr(accept_len),
-                               _ptr(argmax)), "bs_verify")
+    _check(library().bs_verify(h, _ptr(logits), _verify_stride(logits), _ptr(proposals),
+                               _ptr(accept_len), _ptr(argmax)), "bs_verify")
+
+
+def bs_verify_ex(h: int, logits, proposals, top_k: int, min_block: int, accept_len, argmax,
+                 prop_rank=None) -> None:
+    _check(library().bs_verify_ex(h, _ptr(logits), _verify_stride(logits), _ptr(proposals),
+                                  top_k, min_block, _ptr(accept_len), _ptr(argmax),
+                                  _ptr(prop_rank) if prop_rank is not None else None),
+           "bs_verify_ex")
 
 
 def bs_verify_destroy(h: int) -> None:
@@ -304,6 +323,16 @@ class Verifier:
         except Exception:
             pass
 
-    def __call__(self, logits, proposals):
-        bs_verify(self.h, logits, proposals, self.accept_len, self.argmax)
-        return self.accept_len, self.argmax
+    def __call__(self, logits, proposals, top_k=1, min_block=0, rank=False):
+        """Exact verify by default; top_k > 1 or min_block > 1 gives the
+        approximate criteria. With rank=True also returns each proposal's rank."""
+        if top_k == 1 and min_block == 0 and not rank:
+            bs_verify(self.h, logits, proposals, self.accept_len, self.argmax)
+            return self.accept_len, self.argmax
+        import torch
+        rk = None
+        if rank:
+            rk = torch.empty((self.B, self.k), dtype=torch.int32, device=self.argmax.device)
+        bs_verify_ex(self.h, logits, proposals, top_k, min_block, self.accept_len, self.argmax,
+                     rk)
+        return (self.accept_len, self.argmax, rk) if rank else (self.accept_len, self.argmax)

@@ -915,21 +915,33 @@ struct K4Args {
   const void* logits;
   int64_t stride;
   int V, tile, tiles, k, B;
-  float* px;   // [rows][tiles]
-  int* pv;     // [rows][tiles]
+  float* px;   // [rows][tiles] tile maximum
+  int* pv;     // [rows][tiles] its first column
+  int* pc;     // [rows][tiles] logits of the tile that beat the proposal's
   const int32_t* proposals;
   int32_t* accept;
   int32_t* argmax;
+  int32_t* rank;       // optional [rows]
+  int top_k, min_block;
 };
 
-template <typename T, int EPT, bool ALIGNED>
+template <typename T, int EPT, bool ALIGNED, bool COUNT>
 __global__ __launch_bounds__(kThreads) void k4_argmax_tiles(K4Args a) {
   __shared__ float rx[kWaves];
   __shared__ int ri[kWaves];
+  __shared__ int rc[kWaves];
   const int r = blockIdx.y, c = blockIdx.x;
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const int v0 = c * a.tile;
   const int vend = min(a.V, v0 + a.tile);
+  // the proposal's own logit (top-k criterion); an out-of-range proposal is
+  // never read and beaten by nothing here (its rank is set to V later)
+  int prop = -1;
+  float xp = kInf;
+  if (COUNT) {
+    prop = a.proposals[r];
+    if (prop >= 0 && prop < a.V) xp = Elem<T>::load1(row + prop);
+  }
   float x[EPT];
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
   // first index of the maximum; -inf logits take part (padding is excluded)
@@ -958,6 +970,20 @@ __global__ __launch_bounds__(kThreads) void k4_argmax_tiles(K4Args a) {
     ri[wave] = bi;
   }
   __syncthreads();
+  int cnt = 0;
+  if (COUNT && prop >= 0 && prop < a.V) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int v = TileMap<T, ALIGNED>::col(v0, i);
+      cnt += (v < vend && better(x[i], v, xp, prop)) ? 1 : 0;
+    }
+  }
+  if (COUNT) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) rc[wave] = cnt;
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w)
@@ -967,17 +993,22 @@ __global__ __launch_bounds__(kThreads) void k4_argmax_tiles(K4Args a) {
       }
     a.px[(int64_t)r * a.tiles + c] = bx;
     a.pv[(int64_t)r * a.tiles + c] = bi;
+    if (COUNT) a.pc[(int64_t)r * a.tiles + c] = rc[0] + rc[1] + rc[2] + rc[3];
   }
 }
 
-// one wave per item: lane i merges the tiles of position i
+// one wave per item: lane i merges the tiles of position i. Without counts
+// a position passes when its proposal is the argmax; with counts, when the
+// proposal's rank (logits that beat it, summed over tiles) is below top_k.
+template <bool COUNT>
 __global__ __launch_bounds__(64) void k4_accept(K4Args a) {
   const int b = blockIdx.x, i = threadIdx.x;
-  bool match = false;
+  bool pass = false;
   if (i < a.k) {
     const int64_t r = (int64_t)b * a.k + i;
     float bx = -kInf;
     int bi = 0x7fffffff;
+    int rank = 0;
     for (int c = 0; c < a.tiles; ++c) {
       const float x = a.px[r * a.tiles + c];
       const int v = a.pv[r * a.tiles + c];
@@ -985,16 +1016,26 @@ __global__ __launch_bounds__(64) void k4_accept(K4Args a) {
         bx = x;
         bi = v;
       }
+      if (COUNT) rank += a.pc[r * a.tiles + c];
     }
     a.argmax[r] = bi;
-    match = (a.proposals[r] == bi);
+    const int prop = a.proposals[r];
+    if (COUNT) {
+      if (prop < 0 || prop >= a.V) rank = a.V;
+      if (a.rank) a.rank[r] = rank;
+      pass = rank < a.top_k;
+    } else {
+      pass = (prop == bi);
+    }
   }
-  const uint64_t m = __ballot(match);
+  const uint64_t m = __ballot(pass);
   if (i == 0) {
-    // accepted prefix: number of trailing ones of the match mask, at most k
+    // accepted prefix: number of trailing ones of the pass mask, at most k,
+    // and at least the minimum block
     const uint64_t miss = ~m;
     int acc = (miss == 0) ? 64 : __ffsll((long long)miss) - 1;
-    a.accept[b] = acc < a.k ? acc : a.k;
+    acc = acc < a.k ? acc : a.k;
+    a.accept[b] = acc > a.min_block ? acc : a.min_block;
   }
 }
 
@@ -1149,6 +1190,7 @@ struct bs_verify_state {
   void* block;
   float* px;
   int* pv;
+  int* pc;
 };
 
 namespace {
@@ -1256,18 +1298,18 @@ void launch_k5(const K5Args& a, int wmax, hipStream_t s) {
 }
 
 // ---- K4 dispatch ----------------------------------------------------------
-template <typename T, int EPT>
+template <typename T, int EPT, bool COUNT>
 void launch_k4_a(const K4Args& a, bool aligned, dim3 grid, hipStream_t s) {
   if (aligned)
-    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, true, COUNT>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k4_argmax_tiles<T, EPT, false, COUNT>), grid, dim3(kThreads), 0, s, a);
 }
-template <typename T>
+template <typename T, bool COUNT>
 void launch_k4_e(const K4Args& a, int ept, bool aligned, dim3 grid, hipStream_t s) {
-  if (ept == 64) launch_k4_a<T, 64>(a, aligned, grid, s);
-  else if (ept == 32) launch_k4_a<T, 32>(a, aligned, grid, s);
-  else launch_k4_a<T, 16>(a, aligned, grid, s);
+  if (ept == 64) launch_k4_a<T, 64, COUNT>(a, aligned, grid, s);
+  else if (ept == 32) launch_k4_a<T, 32, COUNT>(a, aligned, grid, s);
+  else launch_k4_a<T, 16, COUNT>(a, aligned, grid, s);
 }
 
 int launch_init(bs_state* h) {
@@ -1573,23 +1615,27 @@ int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dty
   h->tile = kThreads * h->ept;
   h->tiles = (vocab + h->tile - 1) / h->tile;
   const size_t pt = (size_t)batch * k * h->tiles;
-  if (hipMalloc(&h->block, 2 * align_up(pt * 4)) != hipSuccess) {
+  if (hipMalloc(&h->block, 3 * align_up(pt * 4)) != hipSuccess) {
     (void)hipGetLastError();
     free(h);
     return BS_ENOMEM;
   }
   h->px = (float*)h->block;
   h->pv = (int*)((char*)h->block + align_up(pt * 4));
+  h->pc = (int*)((char*)h->block + 2 * align_up(pt * 4));
   *out = h;
   return BS_OK;
 }
 
-int bs_verify(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
-              const int32_t* proposals, int32_t* accept_len, int32_t* argmax) {
+int bs_verify_ex(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
+                 const int32_t* proposals, int32_t top_k, int32_t min_block,
+                 int32_t* accept_len, int32_t* argmax, int32_t* prop_rank) {
   if (!h || !logits || !proposals || !accept_len || !argmax) return BS_EINVAL;
-  if (row_stride_elems < h->V) return BS_EINVAL;
+  if (row_stride_elems < h->V || top_k < 1 || min_block < 0 || min_block > h->k)
+    return BS_EINVAL;
   const int esize = h->dtype == BS_BF16 ? 2 : 4;
   const bool aligned = ((uintptr_t)logits % 16 == 0) && ((row_stride_elems * esize) % 16 == 0);
+  const bool count = top_k > 1 || prop_rank != nullptr;
   K4Args a;
   a.logits = logits;
   a.stride = row_stride_elems;
@@ -1600,16 +1646,33 @@ int bs_verify(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
   a.B = h->B;
   a.px = h->px;
   a.pv = h->pv;
+  a.pc = h->pc;
   a.proposals = proposals;
   a.accept = accept_len;
   a.argmax = argmax;
+  a.rank = prop_rank;
+  a.top_k = top_k;
+  a.min_block = min_block;
   dim3 grid(h->tiles, h->B * h->k);
-  if (h->dtype == BS_BF16) launch_k4_e<uint16_t>(a, h->ept, aligned, grid, h->stream);
-  else launch_k4_e<float>(a, h->ept, aligned, grid, h->stream);
+  if (count) {
+    if (h->dtype == BS_BF16) launch_k4_e<uint16_t, true>(a, h->ept, aligned, grid, h->stream);
+    else launch_k4_e<float, true>(a, h->ept, aligned, grid, h->stream);
+  } else {
+    if (h->dtype == BS_BF16) launch_k4_e<uint16_t, false>(a, h->ept, aligned, grid, h->stream);
+    else launch_k4_e<float, false>(a, h->ept, aligned, grid, h->stream);
+  }
   int rc = launch_status();
   if (rc != BS_OK) return rc;
-  hipLaunchKernelGGL(k4_accept, dim3(h->B), dim3(64), 0, h->stream, a);
+  if (count)
+    hipLaunchKernelGGL((k4_accept<true>), dim3(h->B), dim3(64), 0, h->stream, a);
+  else
+    hipLaunchKernelGGL((k4_accept<false>), dim3(h->B), dim3(64), 0, h->stream, a);
   return launch_status();
+}
+
+int bs_verify(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
+              const int32_t* proposals, int32_t* accept_len, int32_t* argmax) {
+  return bs_verify_ex(h, logits, row_stride_elems, proposals, 1, 0, accept_len, argmax, nullptr);
 }
 
 void bs_verify_destroy(bs_verify_state* h) {

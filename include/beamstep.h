@@ -219,6 +219,23 @@ int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dty
 int bs_verify(bs_verify_state *h, const void *logits, int64_t row_stride_elems,
               const int32_t *proposals, int32_t *accept_len, int32_t *argmax);
 
+/* Approximate verify ("Blockwise Parallel Decoding", section 5.1 top-k
+ * selection and section 5.3 minimum block size). Position i passes while the
+ * rank of proposals[b][i] among the logits of row b*k+i is below top_k, the
+ * rank being the number of logits that beat the proposal's (larger, or equal
+ * at a lower index); top_k = 1 is the exact greedy check of bs_verify.
+ * accept_len[b] = max(longest passing prefix, min_block). A proposal outside
+ * [0, V) has rank V and never passes; it is not read.
+ *   top_k      >= 1
+ *   min_block  0..k (0 and 1: no minimum beyond the pages' k^ >= 1)
+ *   prop_rank  device int32 [B][k], written when not NULL
+ * Other arguments as for bs_verify.
+ * Errors: BS_EINVAL (NULL pointer, stride < V, top_k < 1, min_block outside
+ * 0..k); BS_EDEVICE. */
+int bs_verify_ex(bs_verify_state *h, const void *logits, int64_t row_stride_elems,
+                 const int32_t *proposals, int32_t top_k, int32_t min_block,
+                 int32_t *accept_len, int32_t *argmax, int32_t *prop_rank);
+
 void bs_verify_destroy(bs_verify_state *h);
 
 /* Static description of a status code. */

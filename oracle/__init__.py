@@ -67,6 +67,7 @@ def lib():
         L.or_get_hyps.argtypes = [P, i32, P, P, P, P, P, P]
         L.or_kv_reorder.argtypes = [i32, P, i64, i64, i64, i64, i32, i32, i32, P, P]
         L.or_verify.argtypes = [P, i32, i32, i32, i32, i64, P, P, P]
+        L.or_verify_ex.argtypes = [P, i32, i32, i32, i32, i64, P, i32, i32, P, P, P]
         _lib = L
     return _lib
 
@@ -237,3 +238,20 @@ def verify(logits, proposals, dtype: str = "f32"):
     am = np.empty((B, k), np.int32)
     lib().or_verify(_ptr(lg), DTYPES[dtype], B, k, V, V, _ptr(pr), _ptr(acc), _ptr(am))
     return acc, am
+
+
+def verify_ex(logits, proposals, top_k=1, min_block=0, dtype: str = "f32"):
+    """Approximate verify: top-k acceptance and a minimum block size.
+    Returns (accept_len [B], argmax [B, k], rank [B, k])."""
+    want = np.uint16 if dtype == "bf16" else np.float32
+    lg = np.ascontiguousarray(logits, dtype=want)
+    B, k, V = lg.shape
+    pr = np.ascontiguousarray(proposals, dtype=np.int32)
+    acc = np.empty(B, np.int32)
+    am = np.empty((B, k), np.int32)
+    rk = np.empty((B, k), np.int32)
+    rc = lib().or_verify_ex(_ptr(lg), DTYPES[dtype], B, k, V, V, _ptr(pr), top_k, min_block,
+                            _ptr(acc), _ptr(am), _ptr(rk))
+    if rc:
+        raise ValueError("oracle verify_ex: invalid top_k/min_block")
+    return acc, am, rk

@@ -676,3 +676,46 @@ int or_verify(const void *logits, int dtype, int B, int k, int V,
     }
     return 0;
 }
+
+/* Approximate verify ("Blockwise Parallel Decoding" section 5.1, top-k
+ * selection, and section 5.3, minimum block size): position i passes while
+ * the rank of proposals[b][i] among the logits of row b*k+i is below top_k,
+ * the rank being the number of logits that beat the proposal's (larger, or
+ * equal at a lower index), so that top_k = 1 is the exact greedy check;
+ * accept_len = max(longest passing prefix, min(min_block, k)). A proposal
+ * outside [0, V) has rank V. rank may be NULL. */
+int or_verify_ex(const void *logits, int dtype, int B, int k, int V,
+                 int64_t row_stride, const int32_t *proposals, int top_k,
+                 int min_block, int32_t *accept_len, int32_t *argmax,
+                 int32_t *rank)
+{
+    if (top_k < 1 || min_block < 0 || min_block > k)
+        return -1;
+    or_verify(logits, dtype, B, k, V, row_stride, proposals, accept_len, argmax);
+    for (int b = 0; b < B; ++b) {
+        int a = 0, passing = 1;
+        for (int i = 0; i < k; ++i) {
+            int64_t r = (int64_t)b * k + i;
+            int32_t p = proposals[r];
+            int32_t rk = V;
+            if (p >= 0 && p < V) {
+                float xp = logit_at(logits, dtype, row_stride, r, p);
+                rk = 0;
+                for (int v = 0; v < V; ++v) {
+                    float x = logit_at(logits, dtype, row_stride, r, v);
+                    if (x > xp || (x == xp && v < p))
+                        ++rk;
+                }
+            }
+            if (rank)
+                rank[r] = rk;
+            if (passing && rk < top_k)
+                ++a;
+            else
+                passing = 0;
+        }
+        accept_len[b] = a > min_block ? a : min_block;
+    }
+    return 0;
+}
+

@@ -168,6 +168,75 @@ def test_verify_full_size(dev):
     ver.close()
 
 
+def _near_miss_proposals(lg, prop, seed):
+    """Replaces about a third of the proposals by the 2nd..4th best token of
+    their row, so that the top-k criterion has ranks 1..3 to decide on."""
+    rng = np.random.default_rng(seed)
+    x = lg.reshape(-1, lg.shape[-1])
+    p = prop.reshape(-1).copy()
+    pick = np.nonzero(rng.random(p.size) < 0.35)[0]
+    for r in pick:
+        order = np.argsort(-x[r], kind="stable")
+        p[r] = order[rng.integers(1, 4)]
+    return p.reshape(prop.shape).astype(np.int32)
+
+
+def test_verify_topk_min_block_full_size(dev):
+    """Approximate verify (top-k selection, minimum block size) at the full
+    verify shape, against the oracle's ranks and accepted lengths."""
+    import beam_search_step_amd as bs
+    cfg = synth.VERIFY
+    B, k, V = cfg["batch"], cfg["k"], cfg["vocab"]
+    ver = bs.Verifier(B, k, V)
+    lg, prop = synth.verify_inputs(B, k, V, cfg["seed"], call=0)
+    prop = _near_miss_proposals(lg, prop, 5)
+    dlg, dprop = torch.from_numpy(lg).to(dev), torch.from_numpy(prop).to(dev)
+    for top_k, min_block in [(1, 0), (2, 0), (3, 0), (5, 2), (1, 4), (V, 0)]:
+        acc, am, rk = ver(dlg, dprop, top_k=top_k, min_block=min_block, rank=True)
+        oacc, oam, ork = oracle.verify_ex(lg, prop, top_k=top_k, min_block=min_block)
+        assert np.array_equal(rk.cpu().numpy(), ork), (top_k, min_block)
+        assert np.array_equal(am.cpu().numpy(), oam)
+        assert np.array_equal(acc.cpu().numpy(), oacc), (top_k, min_block)
+        log(f"verify top_k={top_k} min_block={min_block}: mean accepted {oacc.mean():.3f}")
+    # without a rank output and top_k > 1 the counting path still runs
+    acc, am = ver(dlg, dprop, top_k=3)
+    assert np.array_equal(acc.cpu().numpy(), oracle.verify_ex(lg, prop, top_k=3)[0])
+    ver.close()
+
+
+def test_verify_topk_edge_cases(dev):
+    """Ties at the proposal's logit, -inf rows, proposals outside [0, V),
+    bf16 and unaligned strides for the counting path."""
+    import beam_search_step_amd as bs
+    rng = np.random.default_rng(17)
+    for (B, k, V, dtype, pad) in [(3, 5, 9, "f32", 0), (2, 3, 4097, "f32", 2),
+                                  (4, 16, 300, "bf16", 0), (1, 8, 70001, "bf16", 5)]:
+        x = rng.integers(-3, 3, size=(B, k, V)).astype(np.float32)   # many ties
+        x[0, 0] = -np.inf
+        if dtype == "bf16":
+            x = synth.f32_to_bf16_bits(x)
+        prop = rng.integers(0, V, size=(B, k)).astype(np.int32)
+        prop[0, 0] = 0
+        prop[-1, -1] = -1 if k > 1 else V
+        prop[0, -1] = V + 7
+        xs = np.zeros((B, k, V + pad), x.dtype)
+        xs[..., :V] = x
+        dx = to_device(xs, dev)[..., :V]
+        ver = bs.Verifier(B, k, V, dtype)
+        for top_k, min_block in [(1, 0), (4, 0), (V // 2, 1), (V, k), (V + 5, 0)]:
+            acc, am, rk = ver(dx, torch.from_numpy(prop).to(dev), top_k=top_k,
+                              min_block=min_block, rank=True)
+            oacc, oam, ork = oracle.verify_ex(x, prop, top_k=top_k, min_block=min_block,
+                                              dtype=dtype)
+            assert np.array_equal(rk.cpu().numpy(), ork), (B, k, V, top_k)
+            assert np.array_equal(am.cpu().numpy(), oam)
+            assert np.array_equal(acc.cpu().numpy(), oacc), (B, k, V, top_k, min_block)
+        for bad in [dict(top_k=0), dict(top_k=1, min_block=k + 1), dict(top_k=1, min_block=-1)]:
+            with pytest.raises(bs.BeamStepError):
+                ver(dx, torch.from_numpy(prop).to(dev), **bad)
+        ver.close()
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------

@@ -428,3 +428,33 @@ def test_kv_reorder_matches_torch_index_select(orc, name, dt):
             src = torch.from_numpy(old.astype(np.int64))
             ref[b * W:(b + 1) * W, P:P + gen] = torch.index_select(src, 0, rows)[:, P:P + gen]
         assert (ref.numpy() == new.astype(np.int64)).all()
+
+
+# ---------------------------------------------------------------------------
+# approximate verify: top-k selection (section 5.1), minimum block (5.3)
+# ---------------------------------------------------------------------------
+def test_verify_topk_and_min_block(orc):
+    # one item, k=4 positions, V=6; the proposal ranks are set by hand
+    lg = np.array([[[0, 9, 1, 2, 3, 4],      # proposal 1 is the argmax: rank 0
+                    [5, 5, 1, 0, 0, 0],      # proposal 1 ties with 0 at 5: rank 1
+                    [1, 2, 3, 4, 5, 6],      # proposal 3: ranks 2 (5 and 6 beat it)
+                    [6, 5, 4, 3, 2, 1]]],    # proposal 5: rank 5
+                  np.float32)
+    prop = np.array([[1, 1, 3, 5]], np.int32)
+    for top_k, want in ((1, 1), (2, 2), (3, 3), (5, 3), (6, 4)):
+        acc, am, rk = orc.verify_ex(lg, prop, top_k=top_k)
+        assert rk[0].tolist() == [0, 1, 2, 5]
+        assert acc[0] == want, (top_k, acc[0])
+    # top_k = 1 is the exact greedy check of the plain verify
+    acc1, am1 = orc.verify(lg, prop)
+    acc2, am2, _ = orc.verify_ex(lg, prop, top_k=1)
+    assert acc1[0] == acc2[0] == 1 and (am1 == am2).all()
+    # minimum block size: at least l tokens are taken, never more than k
+    for ell, want in ((0, 1), (1, 1), (3, 3), (4, 4)):
+        acc, _, _ = orc.verify_ex(lg, prop, top_k=1, min_block=ell)
+        assert acc[0] == want
+    # a proposal outside the vocabulary never passes
+    acc, _, rk = orc.verify_ex(lg, np.array([[7, 1, 3, 5]], np.int32), top_k=6)
+    assert acc[0] == 0 and rk[0, 0] == 6
+    with pytest.raises(ValueError):
+        orc.verify_ex(lg, prop, top_k=0)
