@@ -20,6 +20,7 @@ LIB = os.environ.get("BEAMSTEP_ORACLE_LIB") or os.path.join(HERE, "liboracle.so"
 DTYPES = {"f32": 0, "bf16": 1}
 LPS = {"none": 0, "gnmt": 1, "pow": 2}
 STOPS = {"true": 0, "heuristic": 1, "never": 2}
+PRUNES = {"topw": 0, "top2w": 1}
 
 
 def build(force: bool = True) -> str:
@@ -53,6 +54,7 @@ def lib():
         L.or_create.restype = P
         L.or_create.argtypes = [i32] * 8 + [f64, i32]
         L.or_destroy.argtypes = [P]
+        L.or_set_prune.argtypes = [P, i32]
         L.or_select.argtypes = [P, P, i64]
         L.or_get_selection.argtypes = [P, P, P, P]
         L.or_cand_scores.argtypes = [P, P, i64, i32, i32, P, P]
@@ -93,14 +95,17 @@ class Search:
     """One batched beam search held by the oracle (explicit sequences)."""
 
     def __init__(self, batch, beam, vocab, max_steps, eos_id=-1, pad_id=-1,
-                 dtype="f32", lp="gnmt", alpha=0.6, stop="heuristic"):
+                 dtype="f32", lp="gnmt", alpha=0.6, stop="heuristic", prune="topw"):
         self.B, self.W, self.V, self.T = batch, beam, vocab, max_steps
+        self.K = 2 * beam if prune == "top2w" else beam   # candidates ranked per item
         self.dtype = dtype
         self.pad = pad_id
         self._h = lib().or_create(batch, beam, vocab, max_steps, eos_id, pad_id,
                                   DTYPES[dtype], LPS[lp], alpha, STOPS[stop])
         if not self._h:
             raise ValueError("oracle: invalid search configuration")
+        if prune not in PRUNES or lib().or_set_prune(self._h, PRUNES[prune]):
+            raise ValueError(f"oracle: invalid prune mode {prune!r}")
 
     @classmethod
     def for_workload(cls, wl, **over):
@@ -123,11 +128,12 @@ class Search:
 
     # -- prune -------------------------------------------------------------
     def select(self, logits):
-        """Ranked top-(W+1) of every live item: (j [B,W+1], score, n [B])."""
+        """Ranked top-(K+1) of every live item: (j [B,K+1], score, n [B]),
+        K = W, or 2W for the top2w prune."""
         a = self._logits(logits)
         lib().or_select(self._h, _ptr(a), a.shape[1])
-        j = np.empty((self.B, self.W + 1), np.int64)
-        c = np.empty((self.B, self.W + 1), np.float32)
+        j = np.empty((self.B, self.K + 1), np.int64)
+        c = np.empty((self.B, self.K + 1), np.float32)
         n = np.empty(self.B, np.int32)
         lib().or_get_selection(self._h, _ptr(j), _ptr(c), _ptr(n))
         return j, c, n
@@ -145,8 +151,8 @@ class Search:
                 np.empty((self.B, self.W), np.float32), np.empty(self.B, np.uint8))
 
     def apply(self, sel_j, sel_c):
-        sj = np.ascontiguousarray(sel_j, dtype=np.int64).reshape(self.B, self.W)
-        sc = np.ascontiguousarray(sel_c, dtype=np.float32).reshape(self.B, self.W)
+        sj = np.ascontiguousarray(sel_j, dtype=np.int64).reshape(self.B, self.K)
+        sc = np.ascontiguousarray(sel_c, dtype=np.float32).reshape(self.B, self.K)
         bi, tk, s, d = self._outs()
         rc = lib().or_apply(self._h, _ptr(sj), _ptr(sc), _ptr(bi), _ptr(tk), _ptr(s), _ptr(d))
         if rc:

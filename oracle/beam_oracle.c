@@ -36,8 +36,16 @@
  * widened exactly to fp32 first. Length penalties are evaluated in double and
  * the normalised score is fp32(raw / lp).
  *
+ * Hugging Face variant (or_set_prune, mode 1): the pages' batched code ranks
+ * 2W candidates and skips an EOS ranked W or below ("Transformers中的Beam
+ * Search高效实现", batched section: the rank >= num_beams test and the
+ * break once num_beams beams are filled), which only makes sense with 2W
+ * candidates. Here: take the best 2W; in rank order, an EOS of rank < W
+ * enters the finished set, an EOS of rank >= W is dropped, any other
+ * candidate becomes the next live slot until W slots are filled.
+ *
  * Readings where the pages are silent or disagree (each one is listed with its
- * reason in the design notes): top-W (not 2W) candidates; an EOS selection
+ * reason in the design notes): top-W candidates by default; an EOS selection
  * leaves a dead slot (score -inf) and live selections are compacted in rank
  * order; |y| counts generated tokens including EOS; the stop test runs once
  * per item per step after that step's inserts; "best" in the heuristic test
@@ -151,6 +159,7 @@ typedef struct {
 
 typedef struct or_search {
     int B, W, V, T, eos, pad, dtype, lp, stop;
+    int K;               /* candidates ranked per item: W, or 2W       */
     double alpha;
     int t;               /* steps taken so far                        */
     int finished;        /* or_finish has run                         */
@@ -162,9 +171,9 @@ typedef struct or_search {
     int32_t *hyp_tok;    /* [B][W][T] tokens of the finished set      */
     int32_t *hyp_n;      /* [B]                                       */
     float *lse;          /* [B*W] lse32 of the last select            */
-    int32_t *sel_n;      /* [B] number of finite candidates (<= W+1)  */
-    int64_t *sel_j;      /* [B][W+1] ranked selection                 */
-    float *sel_c;        /* [B][W+1]                                  */
+    int32_t *sel_n;      /* [B] number of finite candidates (<= K+1)  */
+    int64_t *sel_j;      /* [B][K+1] ranked selection                 */
+    float *sel_c;        /* [B][K+1]                                  */
     or_cand *scratch;    /* W*V candidates of one item                */
     int32_t *tmp_seq;    /* [W][T]                                    */
 } or_search;
@@ -199,6 +208,7 @@ or_search *or_create(int B, int W, int V, int T, int eos, int pad, int dtype,
         return NULL;
     o->B = B; o->W = W; o->V = V; o->T = T; o->eos = eos; o->pad = pad;
     o->dtype = dtype; o->lp = lp; o->alpha = alpha; o->stop = stop;
+    o->K = W;
     size_t R = (size_t)B * W;
     o->s = (float *)malloc(R * sizeof(float));
     o->seq = (int32_t *)calloc(R * T, sizeof(int32_t));
@@ -209,8 +219,8 @@ or_search *or_create(int B, int W, int V, int T, int eos, int pad, int dtype,
     o->hyp_n = (int32_t *)calloc(B, sizeof(int32_t));
     o->lse = (float *)calloc(R, sizeof(float));
     o->sel_n = (int32_t *)calloc(B, sizeof(int32_t));
-    o->sel_j = (int64_t *)calloc((size_t)B * (W + 1), sizeof(int64_t));
-    o->sel_c = (float *)calloc((size_t)B * (W + 1), sizeof(float));
+    o->sel_j = (int64_t *)calloc((size_t)B * (2 * W + 1), sizeof(int64_t));
+    o->sel_c = (float *)calloc((size_t)B * (2 * W + 1), sizeof(float));
     o->scratch = (or_cand *)malloc((size_t)W * V * sizeof(or_cand));
     o->tmp_seq = (int32_t *)calloc((size_t)W * T, sizeof(int32_t));
     if (!o->s || !o->seq || !o->slot_rank || !o->done || !o->hyp ||
@@ -225,6 +235,17 @@ or_search *or_create(int B, int W, int V, int T, int eos, int pad, int dtype,
         for (int w = 0; w < W; ++w)
             o->s[b * W + w] = (w == 0) ? 0.0f : -INFINITY;
     return o;
+}
+
+/* Candidates ranked per step: mode 0 the W best (the default), mode 1 the
+ * 2W best with the Hugging Face fill rule (see the header). Only before the
+ * first step. */
+int or_set_prune(or_search *o, int mode)
+{
+    if (o->t != 0 || (mode != 0 && mode != 1))
+        return -1;
+    o->K = mode ? 2 * o->W : o->W;
+    return 0;
 }
 
 /* finished-set order: normalised score desc, then step asc, then rank asc */
@@ -282,18 +303,18 @@ static float hyp_worst_norm(const or_search *o, int b)
 /* prune: the W best of the W*V candidates of every live item          */
 /* ------------------------------------------------------------------ */
 
-/* Fills the ranked selection (top W+1, for near-tie diagnostics) of every
- * item that is not done. Candidates with score -inf (dead rows, -inf logits)
- * are not candidates. */
+/* Fills the ranked selection (top K+1, the extra one for near-tie
+ * diagnostics) of every item that is not done. Candidates with score -inf
+ * (dead rows, -inf logits) are not candidates. */
 int or_select(or_search *o, const void *logits, int64_t row_stride)
 {
-    int B = o->B, W = o->W;
+    int B = o->B, W = o->W, K = o->K;
     int64_t V = o->V;
     for (int b = 0; b < B; ++b) {
         o->sel_n[b] = 0;
-        for (int k = 0; k <= W; ++k) {
-            o->sel_j[(size_t)b * (W + 1) + k] = -1;
-            o->sel_c[(size_t)b * (W + 1) + k] = -INFINITY;
+        for (int k = 0; k <= K; ++k) {
+            o->sel_j[(size_t)b * (K + 1) + k] = -1;
+            o->sel_c[(size_t)b * (K + 1) + k] = -INFINITY;
         }
         if (o->done[b])
             continue;
@@ -319,21 +340,21 @@ int or_select(or_search *o, const void *logits, int64_t row_stride)
             }
         }
         qsort(o->scratch, n, sizeof(or_cand), cand_cmp);
-        int keep = (n < (size_t)(W + 1)) ? (int)n : W + 1;
+        int keep = (n < (size_t)(K + 1)) ? (int)n : K + 1;
         o->sel_n[b] = keep;
         for (int k = 0; k < keep; ++k) {
-            o->sel_j[(size_t)b * (W + 1) + k] = o->scratch[k].j;
-            o->sel_c[(size_t)b * (W + 1) + k] = o->scratch[k].c;
+            o->sel_j[(size_t)b * (K + 1) + k] = o->scratch[k].j;
+            o->sel_c[(size_t)b * (K + 1) + k] = o->scratch[k].c;
         }
     }
     return 0;
 }
 
-/* ranked selection of the last or_select: [B][W+1] flat indices and scores */
+/* ranked selection of the last or_select: [B][K+1] flat indices and scores */
 void or_get_selection(const or_search *o, int64_t *sel_j, float *sel_c,
                       int32_t *sel_n)
 {
-    size_t n = (size_t)o->B * (o->W + 1);
+    size_t n = (size_t)o->B * (o->K + 1);
     memcpy(sel_j, o->sel_j, n * sizeof(int64_t));
     memcpy(sel_c, o->sel_c, n * sizeof(float));
     memcpy(sel_n, o->sel_n, (size_t)o->B * sizeof(int32_t));
@@ -365,14 +386,14 @@ void or_cand_scores(const or_search *o, const void *logits, int64_t row_stride,
 /* finalize: apply a ranked selection                                  */
 /* ------------------------------------------------------------------ */
 
-/* Applies the ranked selection sel_j/sel_c ([B][W], flat index and fp32
+/* Applies the ranked selection sel_j/sel_c ([B][K], flat index and fp32
  * score; j < 0 or score -inf means "no candidate") as the next step. Used
  * with the oracle's own selection, or with another implementation's so that
  * both continue from the same state. Outputs are [B][W] and [B]. */
 int or_apply(or_search *o, const int64_t *sel_j, const float *sel_c,
              int32_t *beam_idx, int32_t *token, float *scores, uint8_t *done_out)
 {
-    int B = o->B, W = o->W, T = o->T;
+    int B = o->B, W = o->W, T = o->T, K = o->K;
     int64_t V = o->V;
     if (o->t >= T || o->finished)
         return -4;
@@ -394,9 +415,9 @@ int or_apply(or_search *o, const int64_t *sel_j, const float *sel_c,
         float new_s[W];
         int32_t new_rank[W];
         float best_raw = -INFINITY;
-        for (int k = 0; k < W; ++k) {
-            int64_t j = sel_j[(size_t)b * W + k];
-            float c = sel_c[(size_t)b * W + k];
+        for (int k = 0; k < K && live < W; ++k) {
+            int64_t j = sel_j[(size_t)b * K + k];
+            float c = sel_c[(size_t)b * K + k];
             if (j < 0 || !(c > -INFINITY))
                 continue;
             if (best_raw == -INFINITY)
@@ -405,6 +426,8 @@ int or_apply(or_search *o, const int64_t *sel_j, const float *sel_c,
             int32_t tok = (int32_t)(j % V);
             const int32_t *pseq = o->seq + ((size_t)b * W + p) * T;
             if (o->eos >= 0 && tok == o->eos) {
+                if (k >= W)
+                    continue; /* 2W variant: an EOS ranked W or below is dropped */
                 int32_t hyp[T];
                 memcpy(hyp, pseq, (size_t)(t - 1) * sizeof(int32_t));
                 hyp[t - 1] = tok;
@@ -466,18 +489,18 @@ int or_step(or_search *o, const void *logits, int64_t row_stride,
     if (o->t >= o->T || o->finished)
         return -4;
     or_select(o, logits, row_stride);
-    int B = o->B, W = o->W;
-    int64_t *j = (int64_t *)malloc((size_t)B * W * sizeof(int64_t));
-    float *c = (float *)malloc((size_t)B * W * sizeof(float));
+    int B = o->B, K = o->K;
+    int64_t *j = (int64_t *)malloc((size_t)B * K * sizeof(int64_t));
+    float *c = (float *)malloc((size_t)B * K * sizeof(float));
     if (!j || !c) {
         free(j);
         free(c);
         return -2;
     }
     for (int b = 0; b < B; ++b)
-        for (int k = 0; k < W; ++k) {
-            j[b * W + k] = o->sel_j[(size_t)b * (W + 1) + k];
-            c[b * W + k] = o->sel_c[(size_t)b * (W + 1) + k];
+        for (int k = 0; k < K; ++k) {
+            j[b * K + k] = o->sel_j[(size_t)b * (K + 1) + k];
+            c[b * K + k] = o->sel_c[(size_t)b * (K + 1) + k];
         }
     int rc = or_apply(o, j, c, beam_idx, token, scores, done_out);
     free(j);

@@ -458,3 +458,78 @@ def test_verify_topk_and_min_block(orc):
     assert acc[0] == 0 and rk[0, 0] == 6
     with pytest.raises(ValueError):
         orc.verify_ex(lg, prop, top_k=0)
+
+
+# ---------------------------------------------------------------------------
+# Hugging Face 2W-candidate variant ("Transformers中的Beam Search高效实现",
+# batched section: 2W candidates, an EOS ranked W or below is skipped, the
+# loop stops once W beams are filled)
+# ---------------------------------------------------------------------------
+def _ln(p):
+    with np.errstate(divide="ignore"):
+        return np.log(np.asarray(p, np.float64)).astype(np.float32)
+
+
+def test_top2w_hand_case(orc):
+    """W=2, V=3 (a=0, b=1, EOS=2), probabilities chosen by hand.
+    Step 1 (row 0): a .55, b .45 -> slots A (a) and B (b).
+    Step 2: after A: a .5, b .1, EOS .4; after B: a .3, b .1, EOS .6.
+    Joint: A a .275, B EOS .27, A EOS .22, B a .135, A b .055, B b .045.
+    top-2W fill: A a live, B EOS (rank 1 < W) finished, A EOS (rank 2) dropped,
+    B a live. top-W: A a live, B EOS finished, slot 1 dead."""
+    W, V, eos = 2, 3, 2
+    step1 = np.stack([_ln([0.55, 0.45, 0.0]), np.zeros(V, np.float32)])
+    step2 = np.stack([_ln([0.5, 0.1, 0.4]), _ln([0.3, 0.1, 0.6])])
+    res = {}
+    for prune in ("top2w", "topw"):
+        o = orc.Search(1, W, V, 3, eos_id=eos, pad_id=-1, lp="none", alpha=0.0, stop="true",
+                       prune=prune)
+        bi, tk, sc, d = o.step(step1)
+        assert bi.tolist() == [[0, 0]] and tk.tolist() == [[0, 1]]
+        res[prune] = o.step(step2) + (o.hyps(0),)
+    bi, tk, sc, d, h = res["top2w"]
+    assert bi.tolist() == [[0, 1]] and tk.tolist() == [[0, 0]] and not d[0]
+    np.testing.assert_allclose(sc[0], np.log([0.275, 0.135]), atol=2e-6)
+    assert len(h) == 1 and h[0]["tokens"] == [1, eos] and h[0]["rank"] == 1
+    assert abs(h[0]["raw"] - math.log(0.27)) < 2e-6
+    bi, tk, sc, d, h = res["topw"]
+    assert bi.tolist() == [[0, 1]] and tk.tolist() == [[0, -1]] and not d[0]
+    assert sc[0, 0] == pytest.approx(math.log(0.275), abs=2e-6) and sc[0, 1] == NEG
+    assert len(h) == 1 and h[0]["tokens"] == [1, eos]
+
+
+def test_top2w_w1_eos_first(orc):
+    """W=1: EOS at rank 0 is finished and rank 1 fills the only beam; with
+    top-W the item has no live beam. Both are done: the one finished
+    hypothesis (ln .6) fills the set and beats the live beam (ln .3)."""
+    x = _ln([0.3, 0.1, 0.6])[None]
+    o = orc.Search(1, 1, 3, 4, eos_id=2, pad_id=-1, lp="none", alpha=0.0, stop="heuristic",
+                   prune="top2w")
+    bi, tk, sc, d = o.step(x)
+    assert tk.tolist() == [[0]] and d[0]
+    assert sc[0, 0] == pytest.approx(math.log(0.3), abs=2e-6)
+    assert [h["tokens"] for h in o.hyps(0)] == [[2]]
+    o = orc.Search(1, 1, 3, 4, eos_id=2, pad_id=-1, lp="none", alpha=0.0, stop="heuristic")
+    bi, tk, sc, d = o.step(x)
+    assert tk.tolist() == [[-1]] and d[0]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_top2w_without_eos_equals_topw(orc, seed):
+    """With no EOS among the candidates the fill rule takes the first W of the
+    2W, which is the top-W selection: both modes must agree at every step."""
+    rng = np.random.default_rng(seed)
+    B, W, V, T = 3, 3, 11, 6
+    a = orc.Search(B, W, V, T, eos_id=-1, lp="gnmt", alpha=0.6, stop="heuristic", prune="top2w")
+    b = orc.Search(B, W, V, T, eos_id=-1, lp="gnmt", alpha=0.6, stop="heuristic")
+    for t in range(T):
+        x = rng.normal(0, 2, size=(B * W, V)).astype(np.float32)
+        ra, rb = a.step(x), b.step(x)
+        for u, v in zip(ra, rb):
+            assert np.array_equal(u, v)
+    assert all(np.array_equal(u, v) for u, v in zip(a.finish(2), b.finish(2)))
+
+
+def test_top2w_rejects_bad_mode(orc):
+    with pytest.raises(ValueError):
+        orc.Search(1, 2, 3, 2, prune="top3w")
