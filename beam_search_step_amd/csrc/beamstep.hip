@@ -253,14 +253,15 @@ struct K1Args {
   const void* logits;
   int64_t stride;       // elements between rows
   int V;
-  int W;                // runtime beam width (<= WMAX)
+  int W;                // beam width: rows per item
+  int K;                // candidates kept per tile (W, or 2W), <= WMAX
   int tile;             // elements per tile (kThreads * EPT)
   int tiles;            // tiles per row
   const float* s;       // running scores [B*W]
   const uint8_t* done;  // [B]
   float* pm;            // [rows][tiles] tile maximum
   float* ps;            // [rows][tiles] sum of exp(x - tile maximum)
-  float* px;            // [rows][tiles][WMAX] tile top-W logits
+  float* px;            // [rows][tiles][WMAX] tile top-K logits
   int* pv;              // [rows][tiles][WMAX] their columns
 };
 
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const int v0 = c * a.tile;
   const int vend = min(a.V, v0 + a.tile);
-  const int W = a.W;
+  const int K = a.K;  // candidates kept per tile
 
   float x[EPT];
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
 
   // prune, stage 1: list every logit >= tau in this wave's LDS region
   // (ballot + mbcnt compaction, no atomics); -inf is never a candidate
-  float tau = tile_tau(gmax, W);
+  float tau = tile_tau(gmax, K);
   if (!(tau > -kInf)) tau = -3.402823466e38f;
   int woff = 0;
 #pragma unroll
@@ -391,13 +392,13 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   }
   float* ox = a.px + pt * WMAX;
   int* oi = a.pv + pt * WMAX;
-  if (tid < WMAX && tid >= min(ntot, W)) {  // ranks without a candidate
+  if (tid < WMAX && tid >= min(ntot, K)) {  // ranks without a candidate
     ox[tid] = -kInf;
     oi[tid] = 0x7fffffff;
   }
   if (!overflow) {
     // rank every listed candidate by counting the better ones, one candidate
-    // per thread over the concatenated regions; the ranks below W go straight
+    // per thread over the concatenated regions; the ranks below K go straight
     // to the tile's output
     int pre[kWaves];
     pre[0] = 0;
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
           rank += (f0 + 3 < n[u] && better(xs.w, is.w, xe, ie)) ? 1 : 0;
         }
       }
-      if (rank < W) {
+      if (rank < K) {
         ox[rank] = xe;
         oi[rank] = ie;
       }
@@ -431,11 +432,11 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
     return;
   }
   // A wave listed more candidates than its region holds (massive ties):
-  // W rounds of a workgroup argmax over the registers, each round taking the
+  // K rounds of a workgroup argmax over the registers, each round taking the
   // best key strictly worse than the previous one. Uniform control flow.
   float px = kInf;
   int pi = -1;
-  for (int rk = 0; rk < W; ++rk) {
+  for (int rk = 0; rk < K; ++rk) {
     float bx = -kInf;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -508,6 +509,7 @@ struct K2Args {
   const float* px;
   const int* pv;
   int B, W, V, T, tiles, eos, pad, stop;
+  int K;               // candidates ranked per item: W, or 2W (Hugging Face fill)
   double alpha;
   int t;               // this step, 1-based
   int32_t* out_beam;
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
   __shared__ int done_sh;
   __shared__ double lp_t, lp_T;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int W = a.W, V = a.V, t = a.t;
+  const int W = a.W, K = a.K, V = a.V, t = a.t;
   const DevState& st = a.st;
   const int bpbase = ((t - 1) * a.B + b) * W;
   const int n_part = W * a.tiles;
@@ -623,8 +625,10 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
       a.out_score[b * W + tid] = -kInf;
       st.bp_par[bpbase + tid] = tid;
       st.bp_tok[bpbase + tid] = a.pad;
-      st.sel_j[b * W + tid] = -1;
-      st.sel_c[b * W + tid] = -kInf;
+    }
+    if (tid < K) {
+      st.sel_j[b * K + tid] = -1;
+      st.sel_c[b * K + tid] = -kInf;
     }
     if (tid == 0) {
       a.out_done[b] = 1;
@@ -674,8 +678,8 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
                                                                    : -kInf;
   __syncthreads();
 
-  // score + prune: each wave keeps the top-W of its lanes' candidates, batch by
-  // batch (the running top-W rides along as one more candidate of lanes < W);
+  // score + prune: each wave keeps the top-K of its lanes' candidates, batch by
+  // batch (the running top-K rides along as one more candidate of lanes < K);
   // then wave 0 merges the waves' lists
   uint64_t carry = 0;
   for (int base = 0; base < n_entries; base += kThreads * kMergeNE) {
@@ -703,33 +707,37 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
       }
     }
     key[kMergeNE] = carry;
-    wave_topw<kMergeNE + 1>(key, W, wave_best[wave]);
-    carry = lane < W ? wave_best[wave][lane] : 0;
+    wave_topw<kMergeNE + 1>(key, K, wave_best[wave]);
+    carry = lane < K ? wave_best[wave][lane] : 0;
   }
   __syncthreads();
 
   if (wave != 0) return;
 
-  // --- wave 0: final top-W, then the finalize sub-step with lane k holding
+  // --- wave 0: final top-K, then the finalize sub-step with lane k holding
   // the rank-k selection
   {
     uint64_t k4[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) k4[w] = lane < W ? wave_best[w][lane] : 0;
-    wave_topw<kWaves>(k4, W, final_best);
+    for (int w = 0; w < kWaves; ++w) k4[w] = lane < K ? wave_best[w][lane] : 0;
+    wave_topw<kWaves>(k4, K, final_best);
   }
-  const uint64_t key = lane < W ? final_best[lane] : 0;
+  const uint64_t key = lane < K ? final_best[lane] : 0;
   const bool valid = key != 0;
   const float c = key_score(key);
   const int j = key_index(key);
   const int p = valid ? j / V : lane;
   const int tok = valid ? j - p * V : a.pad;
-  const bool is_eos = valid && a.eos >= 0 && tok == a.eos;
-  const bool is_live = valid && !is_eos;
+  const bool eos_tok = valid && a.eos >= 0 && tok == a.eos;
+  // an EOS ranked W or below is dropped (only possible with 2W candidates)
+  const bool is_eos = eos_tok && lane < W;
   const uint64_t lt = (lane == 0) ? 0 : (~(uint64_t)0 >> (64 - lane));  // lanes below
+  const uint64_t cand_mask = __ballot(valid && !eos_tok);
+  const int slot = __popcll(cand_mask & lt);  // compacted slot of a live selection
+  // the first W non-EOS candidates in rank order fill the live slots
+  const bool is_live = valid && !eos_tok && slot < W;
   const uint64_t live_mask = __ballot(is_live);
   const uint64_t eos_mask = __ballot(is_eos);
-  const int slot = __popcll(live_mask & lt);  // compacted slot of a live selection
   const int nlive = __popcll(live_mask);
 
   // EOS selections enter the finished set in rank order
@@ -793,6 +801,20 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
 
   // write back: plan, finished set, selection, slots, backpointers
   if (lane < 2 + 3 * kMaxBeam) st.plan[b * kPlanStride + lane] = plan[lane];
+  if (lane < K) {
+    st.sel_j[b * K + lane] = valid ? j : -1;
+    st.sel_c[b * K + lane] = valid ? c : -kInf;
+  }
+  if (is_live) {  // rank `lane` becomes slot `slot`
+    const int r = b * W + slot;
+    st.s[r] = c;
+    st.slot_rank[r] = lane;
+    a.out_beam[r] = p;
+    a.out_tok[r] = tok;
+    a.out_score[r] = c;
+    st.bp_par[bpbase + slot] = p;
+    st.bp_tok[bpbase + slot] = tok;
+  }
   if (lane < W) {
     const int e = b * W + lane;
     st.hnorm[e] = hy.norm[lane];
@@ -802,18 +824,6 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
     st.hrank[e] = hy.rank[lane];
     st.hpar[e] = hy.par[lane];
     st.htok[e] = hy.tok[lane];
-    st.sel_j[e] = valid ? j : -1;
-    st.sel_c[e] = valid ? c : -kInf;
-    if (is_live) {  // rank `lane` becomes slot `slot`
-      const int r = b * W + slot;
-      st.s[r] = c;
-      st.slot_rank[r] = lane;
-      a.out_beam[r] = p;
-      a.out_tok[r] = tok;
-      a.out_score[r] = c;
-      st.bp_par[bpbase + slot] = p;
-      st.bp_tok[bpbase + slot] = tok;
-    }
     if (lane >= nlive) {  // dead slot `lane`
       st.s[e] = -kInf;
       st.slot_rank[e] = W;
@@ -1173,6 +1183,7 @@ struct bs_state {
   hipStream_t stream;
   int device;
   int B, W, V, T, rows, wmax, ept, tile, tiles;
+  int K, kmax;          // candidates ranked per item (W or 2W), pow2 bound
   int t;                // steps taken
   void* block;          // the one device allocation
   DevState st;
@@ -1357,6 +1368,8 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   if (c.tile_elems != 0 && c.tile_elems != 16 && c.tile_elems != 32 && c.tile_elems != 64)
     return BS_EINVAL;
   if (!(c.alpha == c.alpha)) return BS_EINVAL;
+  if (c.prune != BS_PRUNE_TOPW && c.prune != BS_PRUNE_TOP2W) return BS_EINVAL;
+  if (c.prune == BS_PRUNE_TOP2W && 2 * c.beam > kMaxBeam) return BS_EINVAL;
 
   bs_state* h = (bs_state*)calloc(1, sizeof(bs_state));
   if (!h) return BS_ENOMEM;
@@ -1372,6 +1385,8 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   h->T = c.max_steps;
   h->rows = c.batch * c.beam;
   h->wmax = pow2ceil(c.beam);
+  h->K = c.prune == BS_PRUNE_TOP2W ? 2 * c.beam : c.beam;
+  h->kmax = pow2ceil(h->K);
   h->ept = choose_ept(h->rows, c.vocab, c.tile_elems);
   h->tile = kThreads * h->ept;
   h->tiles = (c.vocab + h->tile - 1) / h->tile;
@@ -1386,11 +1401,11 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
       RW * 4, RW * 4, RW * 4, RW * 4, RW * 4, RW * 4, RW * 4,  // finished set
       (size_t)h->B * 4,       // hcount
       BT * 4, BT * 4,         // backpointers
-      RW * 4, RW * 4,         // selection
+      (size_t)h->B * h->K * 4, (size_t)h->B * h->K * 4,  // selection
       (size_t)h->B * kPlanStride * 4,  // plan
       ((size_t)h->T + 1) * 8, // lpt
       PT * 4, PT * 4,         // pm, ps
-      PT * h->wmax * 4, PT * h->wmax * 4,  // px, pv
+      PT * h->kmax * 4, PT * h->kmax * 4,  // px, pv
   };
   const int n = sizeof(sizes) / sizeof(sizes[0]);
   size_t total = 0;
@@ -1462,6 +1477,7 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   a1.stride = row_stride_elems;
   a1.V = h->V;
   a1.W = h->W;
+  a1.K = h->K;
   a1.tile = h->tile;
   a1.tiles = h->tiles;
   a1.s = h->st.s;
@@ -1470,7 +1486,7 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   a1.ps = h->ps;
   a1.px = h->px;
   a1.pv = h->pv;
-  launch_k1(a1, h->wmax, h->cfg.logits_dtype, h->ept, aligned, dim3(h->tiles, h->rows),
+  launch_k1(a1, h->kmax, h->cfg.logits_dtype, h->ept, aligned, dim3(h->tiles, h->rows),
             h->stream);
   int rc = launch_status();
   if (rc != BS_OK) return rc;
@@ -1483,6 +1499,7 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   a2.pv = h->pv;
   a2.B = h->B;
   a2.W = h->W;
+  a2.K = h->K;
   a2.V = h->V;
   a2.T = h->T;
   a2.tiles = h->tiles;
@@ -1495,7 +1512,7 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   a2.out_tok = token_id;
   a2.out_score = scores;
   a2.out_done = done;
-  launch_k2(a2, h->wmax, h->stream);
+  launch_k2(a2, h->kmax, h->stream);
   rc = launch_status();
   if (rc != BS_OK) return rc;
   h->t = t;
@@ -1561,7 +1578,7 @@ int bs_finalize(bs_state* h, int32_t* tokens, int32_t* lengths, float* norm_scor
 int bs_last_selection(bs_state* h, int32_t* flat_idx, float* cand_score) {
   if (!h || !flat_idx || !cand_score) return BS_EINVAL;
   if (h->t == 0) return BS_ESTATE;
-  const size_t n = (size_t)h->rows;
+  const size_t n = (size_t)h->B * h->K;
   if (hipMemcpyAsync(flat_idx, h->st.sel_j, n * 4, hipMemcpyDeviceToDevice, h->stream) !=
           hipSuccess ||
       hipMemcpyAsync(cand_score, h->st.sel_c, n * 4, hipMemcpyDeviceToDevice, h->stream) !=

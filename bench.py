@@ -54,6 +54,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "tbase", "wide", "verify"])
+    ap.add_argument("--prune", default="topw", choices=["topw", "top2w"],
+                    help="top-W candidates, or the Hugging Face 2W-candidate fill")
+    ap.add_argument("--verify-top-k", type=int, default=1,
+                    help="verify: a proposal passes while its rank is below this")
+    ap.add_argument("--verify-min-block", type=int, default=0,
+                    help="verify: minimum accepted block size")
     ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
     ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -115,7 +121,7 @@ def bench_search(args, torch, bs, dev):
           for _ in range(planes_n)]
     desc = bs.make_kv_desc(kv, pos_offset=0)
 
-    g = bs.BeamSearch.for_workload(wl)
+    g = bs.BeamSearch.for_workload(wl, prune=args.prune)
     n_hist = args.steps
     hist_bi = torch.empty((n_hist, B, W), dtype=torch.int32, device=dev)
     hist_tk = torch.empty_like(hist_bi)
@@ -197,8 +203,8 @@ def bench_search(args, torch, bs, dev):
         "config": {
             "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
                         f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
-                        f"gen_len = t",
-            "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype,
+                        f"gen_len = t" + (", 2W-candidate fill" if args.prune == "top2w" else ""),
+            "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype, "prune": args.prune,
             "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
             "logit_pool_buffers": pool_n,
         },
@@ -224,7 +230,7 @@ def bench_search(args, torch, bs, dev):
             "alg_gbs": logit_bytes[1:].sum() / d_step.sum() / 1e9,
         }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
     g.close()
     return out
@@ -250,14 +256,15 @@ def bench_verify(args, torch, bs, dev):
     stream = torch.cuda.current_stream()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps if args.events else 0)]
+    vk = dict(top_k=args.verify_top_k, min_block=args.verify_min_block)
     for i in range(args.warmup):
-        ver(lgs[i % pool_n], props[i % pool_n])
+        ver(lgs[i % pool_n], props[i % pool_n], **vk)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         if args.events:
             events[i][0].record(stream)
-        ver(lgs[i % pool_n], props[i % pool_n])
+        ver(lgs[i % pool_n], props[i % pool_n], **vk)
         if args.events:
             events[i][1].record(stream)
     torch.cuda.synchronize()
@@ -269,8 +276,10 @@ def bench_verify(args, torch, bs, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"blockwise_verify: B={Bv} k={k} V={V} fp32 logits",
-                   "batch": Bv, "k": k, "vocab": V, "logit_pool_buffers": pool_n},
+        "config": {"workload": f"blockwise_verify: B={Bv} k={k} V={V} fp32 logits, "
+                               f"top_k={args.verify_top_k} min_block={args.verify_min_block}",
+                   "batch": Bv, "k": k, "vocab": V, "logit_pool_buffers": pool_n,
+                   "top_k": args.verify_top_k, "min_block": args.verify_min_block},
     }
     if args.events:
         d = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
@@ -279,6 +288,17 @@ def bench_verify(args, torch, bs, dev):
                            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": ach / PEAK_HBM_GBS, "traffic": None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
+    # model calls per generated token implied by the mean accepted block k^
+    # ("Blockwise Parallel Decoding" section 4): separate predict and verify
+    # calls cost 2/k^ per token; merging verify n with predict n+1 costs 1/k^
+    # (plus one call per sequence)
+    khat = float(np.mean([ver(lgs[i], props[i], **vk)[0].float().mean().item()
+                          for i in range(pool_n)]))
+    out["blockwise_accounting"] = {
+        "mean_accepted_block": khat,
+        "model_calls_per_token_separate": 2.0 / khat if khat > 0 else None,
+        "model_calls_per_token_merged": 1.0 / khat if khat > 0 else None,
+    }
     if not args.no_cpu_baseline:
         import oracle
         lg0 = lgs[0].cpu().numpy()
@@ -286,7 +306,7 @@ def bench_verify(args, torch, bs, dev):
         t0 = time.perf_counter()
         n = 0
         while time.perf_counter() - t0 < 2.0:
-            oracle.verify(lg0, pr0)
+            oracle.verify_ex(lg0, pr0, **vk)
             n += 1
         dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": n / dt, "unit": "verify calls/s", "cores": 1,
@@ -340,7 +360,7 @@ def measured_traffic(workload):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, n_steps, bpp, planes_n):
+def cpu_baseline(wl, n_steps, bpp, planes_n, prune="topw"):
     """The CPU oracle, single-threaded on one core, on a bounded sample: the
     first n_steps decode steps of the same search (select + apply over all
     items), each followed by the oracle's KV gather over every plane at
@@ -352,7 +372,7 @@ def cpu_baseline(wl, n_steps, bpp, planes_n):
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     except (AttributeError, OSError):
         pass
-    ref = oracle.Search.for_workload(wl)
+    ref = oracle.Search.for_workload(wl, prune=prune)
     gen = wl.max_steps // 2
     host = [np.zeros((wl.rows, gen, bpp), np.uint8) for _ in range(planes_n)]
     lgs = [synth.logits(wl, t) for t in range(1, n_steps + 1)]

@@ -69,6 +69,15 @@ typedef enum { BS_LP_NONE = 0, BS_LP_GNMT = 1, BS_LP_POW = 2 } bs_lp;
  *                      s / lp(t), s being the best live score. */
 typedef enum { BS_STOP_TRUE = 0, BS_STOP_HEURISTIC = 1, BS_STOP_NEVER = 2 } bs_stop;
 
+/* Candidates ranked per item and step.
+ *   BS_PRUNE_TOPW : the W best of the W*V ("llm_internals" 9.2.2 step 3).
+ *   BS_PRUNE_TOP2W: the Hugging Face form of the batched section of
+ *                   "Transformers中的Beam Search高效实现": the 2W best are
+ *                   ranked; in rank order an EOS of rank < W is finished, an
+ *                   EOS of rank >= W is dropped, and any other candidate fills
+ *                   the next live slot until W are filled. Needs W <= 8. */
+typedef enum { BS_PRUNE_TOPW = 0, BS_PRUNE_TOP2W = 1 } bs_prune;
+
 typedef struct {
     int32_t batch;        /* B >= 1                                        */
     int32_t beam;         /* W, 1..16                                      */
@@ -83,6 +92,7 @@ typedef struct {
     int32_t num_return;   /* hypotheses returned per item, 1..W            */
     int32_t tile_elems;   /* logits per thread in the streaming pass:
                              16, 32 or 64; 0 picks one from B, W, V       */
+    int32_t prune;        /* bs_prune                                      */
 } bs_config;
 
 typedef struct bs_state bs_state;
@@ -180,9 +190,10 @@ int bs_finalize(bs_state *h, int32_t *tokens, int32_t *lengths, float *norm_scor
 
 /* The ranked selection of the last bs_step, before compaction ("prune"
  * output): flat index j (= parent*V + token) and fp32 candidate score, for
- * ranks 0..W-1 of each item; j = -1 and score -inf where an item had fewer
- * than W finite candidates or was already done.
- *   flat_idx  device int32 [B][W];  cand_score  device fp32 [B][W]
+ * ranks 0..K-1 of each item, K = W (BS_PRUNE_TOPW) or 2W (BS_PRUNE_TOP2W);
+ * j = -1 and score -inf where an item had fewer than K finite candidates or
+ * was already done.
+ *   flat_idx  device int32 [B][K];  cand_score  device fp32 [B][K]
  * Errors: BS_EINVAL; BS_ESTATE before the first bs_step. */
 int bs_last_selection(bs_state *h, int32_t *flat_idx, float *cand_score);
 

@@ -49,15 +49,16 @@ def to_device(arr, dev):
     return torch.from_numpy(arr).to(dev)
 
 
-def check_selection(sel, scores_of, gj, gc, W, rep: Report, where: str):
-    """Compare one item's GPU selection (flat j, score) with the oracle's
-    ranked selection ``sel`` = (j [W+1], score [W+1], n); ``scores_of(js)``
-    gives the oracle's fp32 score of arbitrary candidates of the item."""
+def check_selection(sel, scores_of, gj, gc, K, rep: Report, where: str):
+    """Compare one item's GPU selection of K ranked candidates (flat j, score)
+    with the oracle's ranked selection ``sel`` = (j [K+1], score [K+1], n);
+    ``scores_of(js)`` gives the oracle's fp32 score of arbitrary candidates of
+    the item."""
     oj, oc, on = sel
     rep.compared += 1
     valid = gj >= 0
     n_gpu = int(valid.sum())
-    n_ref = int(min(on, W))
+    n_ref = int(min(on, K))
     assert n_gpu == n_ref, f"{where}: {n_gpu} finite selections, oracle {n_ref}"
     assert valid[:n_gpu].all() and not valid[n_gpu:].any(), f"{where}: holes in selection"
     if n_gpu == 0:
@@ -84,14 +85,15 @@ def kv_position(wl, b, slot, pos, plane, words):
 
 
 def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_finished=True,
-                 rep=None, tile_elems=0):
+                 rep=None, tile_elems=0, prune="topw"):
     """Run ``steps`` decode steps of workload ``wl`` on the GPU with the oracle
     following along on ``items`` (default: all; items are independent, so a
     sample of them can be followed at full batch size). With ``kv_planes`` > 0
     a KV cache of that many (layer, K|V) planes, laid out [rows, positions,
     kv_bytes_per_pos], gets position t-1 of every row written and is then
     reordered with gen_len = t each step, and compared bit for bit on the
-    followed items. Returns (Report, gpu search, oracle search)."""
+    followed items. ``prune`` picks the top-W or the 2W-candidate variant on
+    both sides. Returns (Report, gpu search, oracle search)."""
     import torch
     import beam_search_step_amd as bs
 
@@ -99,8 +101,9 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     rep = rep or Report()
     W = wl.beam
-    gpu = bs.BeamSearch.for_workload(wl, tile_elems=tile_elems)
-    ref = oracle.Search.for_workload(wl.replace(batch=len(items)))
+    gpu = bs.BeamSearch.for_workload(wl, tile_elems=tile_elems, prune=prune)
+    ref = oracle.Search.for_workload(wl.replace(batch=len(items)), prune=prune)
+    K = gpu.K
     rows = np.array([b * W + w for b in items for w in range(W)])
     sub = np.array(items)
     words = wl.kv_bytes_per_pos // 4
@@ -119,7 +122,7 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
         for k, b in enumerate(items):
             check_selection((oj[k], oc[k], on[k]),
                             lambda js, k=k: ref.cand_scores(lg_rows, k, js),
-                            gj[b], gc[b], W, rep, f"{where} item {b}")
+                            gj[b], gc[b], K, rep, f"{where} item {b}")
         obi, otk, osc, odn = ref.apply(gj[sub].astype(np.int64), gc[sub])
         assert (bi[sub] == obi).all(), f"{where}: beam_idx {bi[sub]} vs {obi}"
         assert (tk[sub] == otk).all(), f"{where}: token_id {tk[sub]} vs {otk}"

@@ -72,8 +72,9 @@ def test_null_arguments_are_rejected():
 
 
 def test_config_struct_layout_matches_header():
-    # offsets of the C struct on x86-64: eight int32, a double, three int32
+    # offsets of the C struct on x86-64: eight int32, a double, four int32
     assert ctypes.sizeof(bs.bs_config) == 56
     assert bs.bs_config.alpha.offset == 32
     assert bs.bs_config.tile_elems.offset == 48
+    assert bs.bs_config.prune.offset == 52
     assert ctypes.sizeof(bs.bs_kv_desc) == 48

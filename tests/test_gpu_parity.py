@@ -149,6 +149,57 @@ def test_wide_beam_sampled_items(dev, tile_elems):
     g.close()
 
 
+# ---------------------------------------------------------------------------
+# Hugging Face 2W-candidate variant
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("stop", ["heuristic", "true", "never"])
+def test_top2w_toy_with_frequent_eos(dev, seed, stop):
+    wl = synth.WORKLOADS["toy"].replace(seed=seed, eos_in_zipf=False, eos_ramp=2.0,
+                                        ramp_steps=3, stop=stop, num_return=2)
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1, prune="top2w")
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"top2w toy {seed} {stop}")
+    assert any(len(ref.hyps(b)) for b in range(wl.batch)), "no EOS was selected"
+    g.close()
+
+
+@pytest.mark.parametrize("W,V", [(1, 5), (3, 37), (8, 1000), (8, 3)])
+def test_top2w_small_shapes(dev, W, V):
+    """K = 2W up to 16 candidates per item; V < 2W leaves ranks unfilled."""
+    wl = synth.WORKLOADS["toy"].replace(batch=5, beam=W, vocab=V, eos_id=min(2, V - 1),
+                                        eos_in_zipf=False, eos_ramp=1.0, ramp_steps=4,
+                                        lp="gnmt", alpha=0.8, max_steps=9, seed=60 + W,
+                                        num_return=min(W, 3))
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1, prune="top2w")
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"top2w W={W} V={V}")
+    g.close()
+
+
+def test_top2w_transformer_base_sampled(dev):
+    """Transformer-base shape (W=4, so 8 candidates per item) with the EOS
+    schedule, 70 steps, items 2 and 21."""
+    wl = synth.WORKLOADS["tbase"]
+    items = [2, 21]
+    rep, g, ref = run_stepwise(wl, 70, dev, items=items, kv_planes=1, prune="top2w")
+    log(f"top2w tbase: {rep}")
+    assert any(len(ref.hyps(k)) for k in range(len(items))), "no EOS was selected"
+    g.close()
+
+
+def test_top2w_llama3_reachable_eos(dev):
+    wl = synth.WORKLOADS["llama3_8b"].replace(batch=3, eos_id=1, eos_in_zipf=False,
+                                              eos_ramp=14.0, ramp_steps=10, max_steps=20)
+    rep, g, ref = run_stepwise(wl, 20, dev, kv_planes=1, prune="top2w")
+    compare_final(g, ref, range(wl.batch), wl.num_return, "top2w llama3 eos")
+    g.close()
+
+
+def test_top2w_rejects_wide_beam(dev):
+    import beam_search_step_amd as bs
+    with pytest.raises(bs.BeamStepError):
+        bs.BeamSearch(1, 9, 100, 4, prune="top2w")
+
+
 def test_verify_full_size(dev):
     import beam_search_step_amd as bs
     cfg = synth.VERIFY
