@@ -233,23 +233,25 @@ struct TileMap {
 };
 
 template <typename T, int EPT, bool ALIGNED>
-__device__ __forceinline__ void load_tile(const T* row, int v0, int vend, float (&x)[EPT]) {
+__device__ __forceinline__ void load_tile_full(const T* row, int v0, float (&x)[EPT]) {
   constexpr int VEC = TileMap<T, ALIGNED>::kVec;
-  if (v0 + kThreads * EPT <= vend) {
-    // the whole tile is in range (a uniform branch): every load is issued
-    // back to back with no per-element guard, so none waits for another
+  // the whole tile is in range: every load is issued back to back with no
+  // per-element guard, so none waits for another
 #pragma unroll
-    for (int q = 0; q < EPT / VEC; ++q) {
-      const int v = v0 + (q * kThreads + (int)threadIdx.x) * VEC;
-      if (ALIGNED) {
-        Elem<T>::loadv(row + v, &x[q * VEC]);
-      } else {
-        x[q] = Elem<T>::load1(row + v);
-      }
+  for (int q = 0; q < EPT / VEC; ++q) {
+    const int v = v0 + (q * kThreads + (int)threadIdx.x) * VEC;
+    if (ALIGNED) {
+      Elem<T>::loadv(row + v, &x[q * VEC]);
+    } else {
+      x[q] = Elem<T>::load1(row + v);
     }
-    return;
   }
-  // the ragged last tile of a row
+}
+
+// the ragged last tile of a row: columns at or past vend read as -inf
+template <typename T, int EPT, bool ALIGNED>
+__device__ __forceinline__ void load_tile_ragged(const T* row, int v0, int vend, float (&x)[EPT]) {
+  constexpr int VEC = TileMap<T, ALIGNED>::kVec;
 #pragma unroll
   for (int q = 0; q < EPT / VEC; ++q) {
     const int v = v0 + (q * kThreads + (int)threadIdx.x) * VEC;
@@ -261,6 +263,14 @@ __device__ __forceinline__ void load_tile(const T* row, int v0, int vend, float 
         x[q * VEC + k] = (v + k < vend) ? Elem<T>::load1(row + v + k) : -kInf;
     }
   }
+}
+
+template <typename T, int EPT, bool ALIGNED>
+__device__ __forceinline__ void load_tile(const T* row, int v0, int vend, float (&x)[EPT]) {
+  if (v0 + kThreads * EPT <= vend)  // uniform
+    load_tile_full<T, EPT, ALIGNED>(row, v0, x);
+  else
+    load_tile_ragged<T, EPT, ALIGNED>(row, v0, vend, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -318,21 +328,28 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   __shared__ int wn[kWaves];
   __shared__ float rx[kWaves];
   __shared__ int ri[kWaves];
-  __shared__ alignas(16) float lx[kListCap];
-  __shared__ alignas(16) int li[kListCap];
+  __shared__ alignas(16) uint64_t lk[kListCap];  // candidate keys (logit, column)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.y, c = blockIdx.x;
   const int b = r / a.W;
-  const bool skip = a.done[b] != 0;
-  const float sr = a.s[r];
-  if (skip || sr == -kInf) return;  // nothing to expand
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const int v0 = c * a.tile;
   const int vend = min(a.V, v0 + a.tile);
   const int K = a.K;  // candidates kept per tile
 
+  // The row's state and the tile are requested together, and the test waits
+  // for both: a dead row or a finished item costs its (wasted) tile loads, but
+  // a live row's logits are not held back by the state's round trip. An empty
+  // asm with a memory clobber keeps the compiler from sinking the state loads
+  // below the tile's waits. The flag byte is read through its aligned 32-bit
+  // word, a scalar load (the flags array is 256-byte aligned and padded to a
+  // multiple of 256 bytes).
+  const uint32_t done_word = reinterpret_cast<const uint32_t*>(a.done)[b >> 2];
+  const float sr = a.s[r];
+  __asm__ volatile("" ::: "memory");
   float x[EPT];
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
+  if (((done_word >> (8 * (b & 3))) & 0xff) != 0 || sr == -kInf) return;  // nothing to expand
 
   // expand, per wave: the wave maximum mw and sum of exp(x - mw); the 16-lane
   // row maxima double as the group maxima for tau
@@ -364,8 +381,9 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   }
   __syncthreads();
 
-  // prune, stage 1: list every logit >= tau in this wave's LDS region
-  // (ballot + mbcnt compaction, no atomics); -inf is never a candidate
+  // prune, stage 1: list every logit >= tau in this wave's LDS region as a
+  // key that orders by (logit desc, column asc) (ballot + mbcnt compaction, no
+  // atomics); -inf is never a candidate
   float tau = tile_tau(gmax, K);
   if (!(tau > -kInf)) tau = -3.402823466e38f;
   int woff = 0;
@@ -376,10 +394,8 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
     if (bm) {
       const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
                                  (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0));
-      if (cand && pos < kRegion) {
-        lx[wave * kRegion + pos] = x[i];
-        li[wave * kRegion + pos] = TileMap<T, ALIGNED>::col(v0, i);
-      }
+      if (cand && pos < kRegion)
+        lk[wave * kRegion + pos] = pack_key(x[i], TileMap<T, ALIGNED>::col(v0, i));
       woff += __popcll(bm);
     }
   }
@@ -400,11 +416,12 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
     a.pm[pt] = M;
     a.ps[pt] = S;
   }
+  // the list lengths are the same in every lane: keep them in scalar registers
   int n[kWaves], ntot = 0;
   bool overflow = false;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    n[w] = wn[w];
+    n[w] = __builtin_amdgcn_readfirstlane(wn[w]);
     overflow |= n[w] > kRegion;
     ntot += n[w];
   }
@@ -415,9 +432,9 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
     oi[tid] = 0x7fffffff;
   }
   if (!overflow) {
-    // rank every listed candidate by counting the better ones, one candidate
-    // per thread over the concatenated regions; the ranks below K go straight
-    // to the tile's output
+    // rank every listed candidate by counting the larger keys (keys are
+    // unique), one candidate per thread over the concatenated regions, two
+    // keys per LDS read; the ranks below K go straight to the tile's output
     int pre[kWaves];
     pre[0] = 0;
 #pragma unroll
@@ -426,25 +443,21 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
       int w = 0;
 #pragma unroll
       for (int u = 1; u < kWaves; ++u) w = e >= pre[u] ? u : w;
-      const float xe = lx[w * kRegion + e - pre[w]];
-      const int ie = li[w * kRegion + e - pre[w]];
+      const uint64_t mine = lk[w * kRegion + e - pre[w]];
       int rank = 0;
 #pragma unroll
       for (int u = 0; u < kWaves; ++u) {
-        const float* bx = lx + u * kRegion;
-        const int* bi = li + u * kRegion;
-        for (int f0 = 0; f0 < n[u]; f0 += 4) {
-          const float4 xs = *reinterpret_cast<const float4*>(bx + f0);
-          const int4 is = *reinterpret_cast<const int4*>(bi + f0);
-          rank += (f0 + 0 < n[u] && better(xs.x, is.x, xe, ie)) ? 1 : 0;
-          rank += (f0 + 1 < n[u] && better(xs.y, is.y, xe, ie)) ? 1 : 0;
-          rank += (f0 + 2 < n[u] && better(xs.z, is.z, xe, ie)) ? 1 : 0;
-          rank += (f0 + 3 < n[u] && better(xs.w, is.w, xe, ie)) ? 1 : 0;
+        const uint64_t* bl = lk + u * kRegion;
+        int f = 0;
+        for (; f + 2 <= n[u]; f += 2) {
+          const ulonglong2 two = *reinterpret_cast<const ulonglong2*>(bl + f);
+          rank += (two.x > mine ? 1 : 0) + (two.y > mine ? 1 : 0);
         }
+        if (f < n[u]) rank += bl[f] > mine ? 1 : 0;
       }
       if (rank < K) {
-        ox[rank] = xe;
-        oi[rank] = ie;
+        ox[rank] = key_score(mine);
+        oi[rank] = key_index(mine);
       }
     }
     return;
@@ -576,171 +589,39 @@ __device__ void hyp_insert(HypSmem<WMAX>& h, int W, float norm, float raw, int l
   h.tok[slot] = tok;
 }
 
+// A finished item's step: no selection, every slot keeps itself, nothing to
+// reorder.
+__device__ __forceinline__ void noop_item(const K2Args& a, int b, int tid) {
+  const int W = a.W, K = a.K;
+  const DevState& st = a.st;
+  const int bpbase = ((a.t - 1) * a.B + b) * W;
+  if (tid < W) {
+    a.out_beam[b * W + tid] = tid;
+    a.out_tok[b * W + tid] = a.pad;
+    a.out_score[b * W + tid] = -kInf;
+    st.bp_par[bpbase + tid] = tid;
+    st.bp_tok[bpbase + tid] = a.pad;
+  }
+  if (tid < K) {
+    st.sel_j[b * K + tid] = -1;
+    st.sel_c[b * K + tid] = -kInf;
+  }
+  if (tid == 0) {
+    a.out_done[b] = 1;
+    st.plan[b * kPlanStride + 1] = 0;
+  }
+}
+
+// The finalize sub-step of item b, run by wave 0 with lane k holding the
+// rank-k selected key (0 = none): EOS selections into the finished set in rank
+// order, compaction of the live slots, the stop rule, the KV reorder plan, and
+// the write-back of outputs, state and backpointers.
 template <int WMAX>
-__global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
-  constexpr int kStage = 4 * kThreads;  // tile partials staged per pass
-  __shared__ HypSmem<WMAX> hy;
-  __shared__ float lse[WMAX];
-  __shared__ float srow[WMAX];
-  __shared__ float stage_m[kStage], stage_s[kStage];
-  __shared__ float lse_m[WMAX], lse_s[WMAX];
-  __shared__ uint64_t wave_best[kWaves][WMAX];
-  __shared__ uint64_t final_best[WMAX];
-  __shared__ int plan[kPlanStride];
-  __shared__ int done_sh;
-  __shared__ double lp_t, lp_T;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void finalize_item(const K2Args& a, HypSmem<WMAX>& hy, int* plan, int b,
+                                              int lane, uint64_t key, double lp_t, double lp_T) {
   const int W = a.W, K = a.K, V = a.V, t = a.t;
   const DevState& st = a.st;
   const int bpbase = ((t - 1) * a.B + b) * W;
-  const int n_part = W * a.tiles;
-  const int per_row = a.tiles * WMAX;
-  const int n_entries = W * per_row;
-  const float* px = a.px + (int64_t)b * n_entries;
-  const int* pv = a.pv + (int64_t)b * n_entries;
-
-  // every load of the item's state and of the first batch is issued up front
-  float lx[kMergeNE];
-  int lv[kMergeNE];
-#pragma unroll
-  for (int q = 0; q < kMergeNE; ++q) {
-    const int e = q * kThreads + tid;
-    lx[q] = e < n_entries ? px[e] : -kInf;
-    lv[q] = e < n_entries ? pv[e] : 0;
-  }
-  for (int k = 0; k < kStage / kThreads; ++k) {
-    const int e = k * kThreads + tid;
-    if (e < n_part) {
-      stage_m[e] = a.pm[(int64_t)b * n_part + e];
-      stage_s[e] = a.ps[(int64_t)b * n_part + e];
-    }
-  }
-  if (tid < W) {
-    const int e = b * W + tid;
-    srow[tid] = st.s[e];
-    hy.norm[tid] = st.hnorm[e];
-    hy.raw[tid] = st.hraw[e];
-    hy.len[tid] = st.hlen[e];
-    hy.step[tid] = st.hstep[e];
-    hy.rank[tid] = st.hrank[e];
-    hy.par[tid] = st.hpar[e];
-    hy.tok[tid] = st.htok[e];
-    lse_m[tid] = -kInf;
-    lse_s[tid] = 0.0f;
-  }
-  if (tid == 0) {
-    done_sh = st.done[b];
-    hy.count = st.hcount[b];
-    lp_t = st.lpt[t];
-    lp_T = st.lpt[a.T];
-  }
-  __syncthreads();
-
-  if (done_sh) {  // finished items: no-op outputs
-    if (tid < W) {
-      a.out_beam[b * W + tid] = tid;
-      a.out_tok[b * W + tid] = a.pad;
-      a.out_score[b * W + tid] = -kInf;
-      st.bp_par[bpbase + tid] = tid;
-      st.bp_tok[bpbase + tid] = a.pad;
-    }
-    if (tid < K) {
-      st.sel_j[b * K + tid] = -1;
-      st.sel_c[b * K + tid] = -kInf;
-    }
-    if (tid == 0) {
-      a.out_done[b] = 1;
-      st.plan[b * kPlanStride + 1] = 0;
-    }
-    return;
-  }
-
-  // expand: lse of every live row from its tile partials. One wave per row,
-  // lanes over tiles: the row maximum, then sum of S_tile * exp(M_tile - M),
-  // both with fixed reduction trees.
-  for (int base = 0; base < n_part; base += kStage) {
-    if (base > 0) {
-      __syncthreads();
-      for (int k = 0; k < kStage / kThreads; ++k) {
-        const int e = base + k * kThreads + tid;
-        if (e < n_part) {
-          stage_m[e - base] = a.pm[(int64_t)b * n_part + e];
-          stage_s[e - base] = a.ps[(int64_t)b * n_part + e];
-        }
-      }
-      __syncthreads();
-    }
-    for (int w = wave; w < W; w += kWaves) {
-      if (!(srow[w] > -kInf)) continue;
-      const int lo = max(base, w * a.tiles), hi = min(base + kStage, (w + 1) * a.tiles);
-      float m = -kInf;
-      for (int e = lo + lane; e < hi; e += 64) m = fmaxf(m, stage_m[e - base]);
-      m = wave_max_f(m);
-      float sum = 0.0f;
-      if (m > -kInf)
-        for (int e = lo + lane; e < hi; e += 64) {
-          const float mt = stage_m[e - base];
-          if (mt > -kInf) sum += stage_s[e - base] * exp2f((mt - m) * kLog2e);
-        }
-      sum = wave_sum_f(sum);
-      if (lane == 0) {  // combine with the previous pass (tiles beyond kStage)
-        float pm = lse_m[w], ps = lse_s[w];
-        lse_combine(pm, ps, m, sum);
-        lse_m[w] = pm;
-        lse_s[w] = ps;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid < W) lse[tid] = (srow[tid] > -kInf && lse_m[tid] > -kInf) ? lse_m[tid] + logf(lse_s[tid])
-                                                                   : -kInf;
-  __syncthreads();
-
-  // score + prune: each wave keeps the top-K of its lanes' candidates, batch by
-  // batch (the running top-K rides along as one more candidate of lanes < K);
-  // then wave 0 merges the waves' lists
-  uint64_t carry = 0;
-  for (int base = 0; base < n_entries; base += kThreads * kMergeNE) {
-    if (base > 0) {
-#pragma unroll
-      for (int q = 0; q < kMergeNE; ++q) {
-        const int e = base + q * kThreads + tid;
-        lx[q] = e < n_entries ? px[e] : -kInf;
-        lv[q] = e < n_entries ? pv[e] : 0;
-      }
-    }
-    uint64_t key[kMergeNE + 1];
-#pragma unroll
-    for (int q = 0; q < kMergeNE; ++q) {
-      const int e = base + q * kThreads + tid;
-      key[q] = 0;
-      if (e < n_entries) {
-        const int w = e / per_row;
-        const float lw = lse[w];
-        if (lx[q] > -kInf && lw > -kInf) {
-          const float logp = lx[q] - lw;   // fp32 log-probability
-          const float c = srow[w] + logp;  // fp32 candidate score
-          if (c > -kInf) key[q] = pack_key(c, w * V + lv[q]);
-        }
-      }
-    }
-    key[kMergeNE] = carry;
-    wave_topw<kMergeNE + 1>(key, K, wave_best[wave]);
-    carry = lane < K ? wave_best[wave][lane] : 0;
-  }
-  __syncthreads();
-
-  if (wave != 0) return;
-
-  // --- wave 0: final top-K, then the finalize sub-step with lane k holding
-  // the rank-k selection
-  {
-    uint64_t k4[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) k4[w] = lane < K ? wave_best[w][lane] : 0;
-    wave_topw<kWaves>(k4, K, final_best);
-  }
-  const uint64_t key = lane < K ? final_best[lane] : 0;
   const bool valid = key != 0;
   const float c = key_score(key);
   const int j = key_index(key);
@@ -851,6 +732,402 @@ __global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
       st.bp_tok[bpbase + lane] = a.pad;
     }
   }
+}
+
+// K2 for any tile count (the path for rows of more than 64 tiles): every
+// listed candidate is scored, and each wave keeps its lanes' top-K by K rounds
+// of a wave maximum, batch by batch; wave 0 merges the four lists.
+template <int WMAX>
+__global__ __launch_bounds__(kThreads) void k2_merge_finalize(K2Args a) {
+  constexpr int kStage = 4 * kThreads;  // tile partials staged per pass
+  __shared__ HypSmem<WMAX> hy;
+  __shared__ float lse[WMAX];
+  __shared__ float srow[WMAX];
+  __shared__ float stage_m[kStage], stage_s[kStage];
+  __shared__ float lse_m[WMAX], lse_s[WMAX];
+  __shared__ uint64_t wave_best[kWaves][WMAX];
+  __shared__ uint64_t final_best[WMAX];
+  __shared__ int plan[kPlanStride];
+  __shared__ int done_sh;
+  __shared__ double lp_t, lp_T;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = a.W, K = a.K, V = a.V, t = a.t;
+  const DevState& st = a.st;
+  const int n_part = W * a.tiles;
+  const int per_row = a.tiles * WMAX;
+  const int n_entries = W * per_row;
+  const float* px = a.px + (int64_t)b * n_entries;
+  const int* pv = a.pv + (int64_t)b * n_entries;
+
+  // every load of the item's state and of the first batch is issued up front
+  float lx[kMergeNE];
+  int lv[kMergeNE];
+#pragma unroll
+  for (int q = 0; q < kMergeNE; ++q) {
+    const int e = q * kThreads + tid;
+    lx[q] = e < n_entries ? px[e] : -kInf;
+    lv[q] = e < n_entries ? pv[e] : 0;
+  }
+  for (int k = 0; k < kStage / kThreads; ++k) {
+    const int e = k * kThreads + tid;
+    if (e < n_part) {
+      stage_m[e] = a.pm[(int64_t)b * n_part + e];
+      stage_s[e] = a.ps[(int64_t)b * n_part + e];
+    }
+  }
+  if (tid < W) {
+    const int e = b * W + tid;
+    srow[tid] = st.s[e];
+    hy.norm[tid] = st.hnorm[e];
+    hy.raw[tid] = st.hraw[e];
+    hy.len[tid] = st.hlen[e];
+    hy.step[tid] = st.hstep[e];
+    hy.rank[tid] = st.hrank[e];
+    hy.par[tid] = st.hpar[e];
+    hy.tok[tid] = st.htok[e];
+    lse_m[tid] = -kInf;
+    lse_s[tid] = 0.0f;
+  }
+  if (tid == 0) {
+    done_sh = st.done[b];
+    hy.count = st.hcount[b];
+    lp_t = st.lpt[t];
+    lp_T = st.lpt[a.T];
+  }
+  __syncthreads();
+
+  if (done_sh) {  // finished items: no-op outputs
+    noop_item(a, b, tid);
+    return;
+  }
+
+  // expand: lse of every live row from its tile partials. One wave per row,
+  // lanes over tiles: the row maximum, then sum of S_tile * exp(M_tile - M),
+  // both with fixed reduction trees.
+  for (int base = 0; base < n_part; base += kStage) {
+    if (base > 0) {
+      __syncthreads();
+      for (int k = 0; k < kStage / kThreads; ++k) {
+        const int e = base + k * kThreads + tid;
+        if (e < n_part) {
+          stage_m[e - base] = a.pm[(int64_t)b * n_part + e];
+          stage_s[e - base] = a.ps[(int64_t)b * n_part + e];
+        }
+      }
+      __syncthreads();
+    }
+    for (int w = wave; w < W; w += kWaves) {
+      if (!(srow[w] > -kInf)) continue;
+      const int lo = max(base, w * a.tiles), hi = min(base + kStage, (w + 1) * a.tiles);
+      float m = -kInf;
+      for (int e = lo + lane; e < hi; e += 64) m = fmaxf(m, stage_m[e - base]);
+      m = wave_max_f(m);
+      float sum = 0.0f;
+      if (m > -kInf)
+        for (int e = lo + lane; e < hi; e += 64) {
+          const float mt = stage_m[e - base];
+          if (mt > -kInf) sum += stage_s[e - base] * exp2f((mt - m) * kLog2e);
+        }
+      sum = wave_sum_f(sum);
+      if (lane == 0) {  // combine with the previous pass (tiles beyond kStage)
+        float pm = lse_m[w], ps = lse_s[w];
+        lse_combine(pm, ps, m, sum);
+        lse_m[w] = pm;
+        lse_s[w] = ps;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < W) lse[tid] = (srow[tid] > -kInf && lse_m[tid] > -kInf) ? lse_m[tid] + logf(lse_s[tid])
+                                                                   : -kInf;
+  __syncthreads();
+
+  // score + prune: each wave keeps the top-K of its lanes' candidates, batch by
+  // batch (the running top-K rides along as one more candidate of lanes < K);
+  // then wave 0 merges the waves' lists
+  uint64_t carry = 0;
+  for (int base = 0; base < n_entries; base += kThreads * kMergeNE) {
+    if (base > 0) {
+#pragma unroll
+      for (int q = 0; q < kMergeNE; ++q) {
+        const int e = base + q * kThreads + tid;
+        lx[q] = e < n_entries ? px[e] : -kInf;
+        lv[q] = e < n_entries ? pv[e] : 0;
+      }
+    }
+    uint64_t key[kMergeNE + 1];
+#pragma unroll
+    for (int q = 0; q < kMergeNE; ++q) {
+      const int e = base + q * kThreads + tid;
+      key[q] = 0;
+      if (e < n_entries) {
+        const int w = e / per_row;
+        const float lw = lse[w];
+        if (lx[q] > -kInf && lw > -kInf) {
+          const float logp = lx[q] - lw;   // fp32 log-probability
+          const float c = srow[w] + logp;  // fp32 candidate score
+          if (c > -kInf) key[q] = pack_key(c, w * V + lv[q]);
+        }
+      }
+    }
+    key[kMergeNE] = carry;
+    wave_topw<kMergeNE + 1>(key, K, wave_best[wave]);
+    carry = lane < K ? wave_best[wave][lane] : 0;
+  }
+  __syncthreads();
+
+  if (wave != 0) return;
+
+  // --- wave 0: final top-K, then the finalize sub-step
+  uint64_t key;
+  {
+    uint64_t k4[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) k4[w] = lane < K ? wave_best[w][lane] : 0;
+    wave_topw<kWaves>(k4, K, final_best);
+    key = lane < K ? final_best[lane] : 0;
+  }
+  finalize_item<WMAX>(a, hy, plan, b, lane, key, lp_t, lp_T);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_f(float v) { return fmaxf(v, dpp_f<CTRL>(v)); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_f(float v) { return v + dpp_f<CTRL>(v); }
+
+// Maximum over each aligned group of 16 lanes (a DPP row); every lane of the
+// row ends with it.
+__device__ __forceinline__ float row16_max_f(float v) {
+  v = dpp_max_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_f<0x141>(v);  // row_half_mirror
+  v = dpp_max_f<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_sum_f(float v) {
+  v = dpp_add_f<0xb1>(v);
+  v = dpp_add_f<0x4e>(v);
+  v = dpp_add_f<0x141>(v);
+  v = dpp_add_f<0x140>(v);
+  return v;
+}
+
+// K2 for tiles <= 64: merge + score + prune + finalize, one workgroup per item.
+//
+// Stage A, per row: every tile list is ordered by logit, hence by candidate
+// score, so K rounds of a merge of the row's tile lists give the row's best K.
+// A 16-lane row of the wave serves one beam row; lane l holds the lists of
+// tiles l*H .. l*H+H-1 as scores and columns in registers. Each round takes
+// the maximum head score over the 16 lanes (DPP), the ballot of the lanes
+// holding it, and the lowest such lane: lower lanes hold lower tiles, hence
+// lower columns, so ties go to the lower flat index. That lane emits its head
+// and moves to its next entry.
+// Stage B, wave 0: the W row lists are merged the same way (lane w holds row
+// w's list; a lower row means a lower flat index), and the K winners are put
+// in exact (score desc, flat index asc) order before the finalize.
+template <int WMAX, int H>
+__global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
+  __shared__ HypSmem<WMAX> hy;
+  __shared__ float row_sc[kMaxBeam][WMAX];  // each row's best K, merge order
+  __shared__ int row_j[kMaxBeam][WMAX];
+  __shared__ uint64_t ordered[WMAX];
+  __shared__ int plan[kPlanStride];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = a.W, K = a.K, V = a.V, tiles = a.tiles;
+  const DevState& st = a.st;
+  const int w = tid >> 4;   // beam row of this lane's 16-lane group
+  const int gl = tid & 15;  // lane within the group
+  const int c0 = gl * H;    // first tile of this lane
+
+  // every load of the item is issued before the first wait: the finished set,
+  // the flags and length penalties, and the partials of the lane's tiles
+  float h_norm = 0.0f, h_raw = 0.0f;
+  int h_len = 0, h_step = 0, h_rank = 0, h_par = 0, h_tok = 0;
+  if (tid < W) {
+    const int e = b * W + tid;
+    h_norm = st.hnorm[e];
+    h_raw = st.hraw[e];
+    h_len = st.hlen[e];
+    h_step = st.hstep[e];
+    h_rank = st.hrank[e];
+    h_par = st.hpar[e];
+    h_tok = st.htok[e];
+  }
+  const int done = st.done[b];
+  const int hcount = st.hcount[b];
+  const double lp_t = st.lpt[a.t], lp_T = st.lpt[a.T];
+
+  float sr = -kInf;
+  float tm[H], ts[H];
+  float sc[H][WMAX];
+  int col[H][WMAX];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    tm[h] = -kInf;
+    ts[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      sc[h][i] = -kInf;
+      col[h][i] = 0;
+    }
+  }
+  if (w < W) {
+    sr = st.s[b * W + w];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      if (c0 + h < tiles) {
+        const int64_t pt = (int64_t)(b * W + w) * tiles + c0 + h;
+        tm[h] = a.pm[pt];
+        ts[h] = a.ps[pt];
+#pragma unroll
+        for (int i = 0; i < WMAX; ++i) {
+          sc[h][i] = a.px[pt * WMAX + i];
+          col[h][i] = a.pv[pt * WMAX + i];
+        }
+      }
+    }
+  }
+  // dead rows (and rows the expand pass skipped) take no part
+  const bool live = w < W && sr > -kInf;
+  // lse of row w from its tiles' (max, sum exp) partials
+  float m = -kInf;
+#pragma unroll
+  for (int h = 0; h < H; ++h) m = fmaxf(m, live ? tm[h] : -kInf);
+  m = row16_max_f(m);
+  float e = 0.0f;
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+    if (live && tm[h] > -kInf) e += ts[h] * exp2f((tm[h] - m) * kLog2e);
+  e = row16_sum_f(e);
+  const float lse = m > -kInf ? m + logf(e) : -kInf;
+  // candidate scores cand = fp32(s + fp32(x - lse)); -inf is no candidate.
+  // Entries K.. of a tile list are -inf; K rounds could not reach them anyway
+  // (K better entries of the same tile come first).
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      float c = -kInf;
+      if (live && lse > -kInf && sc[h][i] > -kInf) {
+        const float logp = sc[h][i] - lse;
+        c = sr + logp;
+      }
+      sc[h][i] = c;
+    }
+
+  // stage A: K rounds per row
+  {
+    const uint64_t below = ((uint64_t)1 << (lane & 15)) - 1;  // lower lanes of the group
+    const int gshift = lane & 48;
+    float hs[H];
+    int hc[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      hs[h] = sc[h][0];
+      hc[h] = col[h][0];
+    }
+    for (int r = 0; r < K; ++r) {
+      // this lane's best head: the first of its tiles holding the maximum
+      int bh = 0;
+      float bs = hs[0];
+#pragma unroll
+      for (int h = 1; h < H; ++h)
+        if (hs[h] > bs) {
+          bs = hs[h];
+          bh = h;
+        }
+      const float M = row16_max_f(bs);
+      const uint64_t holders = __ballot(bs == M && M > -kInf);
+      const bool win = bs == M && M > -kInf && ((holders >> gshift) & below) == 0;
+      if (gl == 0 && w < W && !(M > -kInf)) {  // the row has no candidate left
+        row_sc[w][r] = -kInf;
+        row_j[w][r] = 0;
+      }
+      if (win) {
+        int hcol = hc[0];
+#pragma unroll
+        for (int h = 1; h < H; ++h) hcol = bh == h ? hc[h] : hcol;
+        row_sc[w][r] = M;
+        row_j[w][r] = w * V + hcol;
+        // the winning list moves up by one entry (register moves: the lists
+        // are never indexed at run time)
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          if (bh == h) {
+#pragma unroll
+            for (int i = 0; i + 1 < WMAX; ++i) {
+              sc[h][i] = sc[h][i + 1];
+              col[h][i] = col[h][i + 1];
+            }
+            sc[h][WMAX - 1] = -kInf;
+            hs[h] = sc[h][0];
+            hc[h] = col[h][0];
+          }
+        }
+      }
+    }
+  }
+  if (tid < W) {
+    hy.norm[tid] = h_norm;
+    hy.raw[tid] = h_raw;
+    hy.len[tid] = h_len;
+    hy.step[tid] = h_step;
+    hy.rank[tid] = h_rank;
+    hy.par[tid] = h_par;
+    hy.tok[tid] = h_tok;
+  }
+  if (tid == 0) hy.count = hcount;
+  __syncthreads();
+
+  if (done) {  // finished items: no-op outputs
+    noop_item(a, b, tid);
+    return;
+  }
+  if (wave != 0) return;
+
+  // stage B: lane w < W holds row w's list; lane r keeps round r's winner
+  float rs[WMAX];
+  int rj[WMAX];
+#pragma unroll
+  for (int i = 0; i < WMAX; ++i) {
+    const bool in = lane < W && i < K;
+    rs[i] = in ? row_sc[lane < W ? lane : 0][i] : -kInf;
+    rj[i] = in ? row_j[lane < W ? lane : 0][i] : 0;
+  }
+  float hs = rs[0], fs = -kInf;
+  int hj = rj[0], fj = 0;
+  for (int r = 0; r < K; ++r) {
+    const float M = row16_max_f(hs);  // lanes 0..15 hold every row
+    const uint64_t holders = __ballot(lane < 16 && hs == M && M > -kInf);
+    if (holders == 0) break;  // uniform: no candidate left
+    const int l = __builtin_ctzll(holders);
+    const int wj = __builtin_amdgcn_readlane(hj, l);
+    if (lane == r) {
+      fs = M;
+      fj = wj;
+    }
+    if (lane == l) {  // the winning row's list moves up by one entry
+#pragma unroll
+      for (int i = 0; i + 1 < WMAX; ++i) {
+        rs[i] = rs[i + 1];
+        rj[i] = rj[i + 1];
+      }
+      rs[WMAX - 1] = -kInf;
+      hs = rs[0];
+      hj = rj[0];
+    }
+  }
+  // exact order of the K winners: rank = number of better winners (the empty
+  // ranks come last and keep their places)
+  const uint64_t fk = fs > -kInf ? pack_key(fs, fj) : 0;
+  int rank = 0;
+  for (int q = 0; q < K; ++q) rank += readlane_u64(fk, q) > fk ? 1 : 0;
+  if (fk == 0) rank = lane;
+  if (lane < K) ordered[rank] = fk;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const uint64_t key = lane < K ? ordered[lane] : 0;
+  finalize_item<WMAX>(a, hy, plan, b, lane, key, lp_t, lp_T);
 }
 
 // ---------------------------------------------------------------------------
@@ -1310,6 +1587,21 @@ void launch_k1(const K1Args& a, int wmax, int dtype, int ept, bool aligned, dim3
 
 void launch_k2(const K2Args& a, int wmax, hipStream_t s) {
   dim3 g(a.B), blk(kThreads);
+  if (a.tiles <= 64) {
+    const int H = a.tiles <= 16 ? 1 : (a.tiles <= 32 ? 2 : 4);  // tiles per lane
+    switch (wmax * 8 + H) {
+#define K2SEL(WM, HH) \
+  case WM * 8 + HH: hipLaunchKernelGGL((k2_select_finalize<WM, HH>), g, blk, 0, s, a); break;
+      K2SEL(1, 1) K2SEL(1, 2) K2SEL(1, 4)
+      K2SEL(2, 1) K2SEL(2, 2) K2SEL(2, 4)
+      K2SEL(4, 1) K2SEL(4, 2) K2SEL(4, 4)
+      K2SEL(8, 1) K2SEL(8, 2) K2SEL(8, 4)
+      K2SEL(16, 1) K2SEL(16, 2) K2SEL(16, 4)
+#undef K2SEL
+      default: break;
+    }
+    return;
+  }
   switch (wmax) {
     case 1: hipLaunchKernelGGL((k2_merge_finalize<1>), g, blk, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k2_merge_finalize<2>), g, blk, 0, s, a); break;

@@ -60,6 +60,8 @@ def parse():
                     help="verify: a proposal passes while its rank is below this")
     ap.add_argument("--verify-min-block", type=int, default=0,
                     help="verify: minimum accepted block size")
+    ap.add_argument("--tile-elems", type=int, default=0, choices=[0, 16, 32, 64],
+                    help="logits per thread in the streaming pass (0: the library's choice)")
     ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
     ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,7 +123,7 @@ def bench_search(args, torch, bs, dev):
           for _ in range(planes_n)]
     desc = bs.make_kv_desc(kv, pos_offset=0)
 
-    g = bs.BeamSearch.for_workload(wl, prune=args.prune)
+    g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems)
     n_hist = args.steps
     hist_bi = torch.empty((n_hist, B, W), dtype=torch.int32, device=dev)
     hist_tk = torch.empty_like(hist_bi)
