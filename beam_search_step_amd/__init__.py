@@ -47,6 +47,14 @@ class bs_kv_desc(ctypes.Structure):
     ]
 
 
+class bs_kv_pool(ctypes.Structure):
+    _fields_ = [
+        ("n_planes", ctypes.c_int32), ("pools", ctypes.POINTER(ctypes.c_void_p)),
+        ("block_stride", ctypes.c_int64), ("pos_stride", ctypes.c_int64),
+        ("bytes_per_pos", ctypes.c_int64),
+    ]
+
+
 class BeamStepError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = status
@@ -76,6 +84,13 @@ def library() -> ctypes.CDLL:
         L.bs_steps_taken.argtypes = [P]
         L.bs_destroy.argtypes = [P]
         L.bs_destroy.restype = None
+        L.bs_kv_paged_create.argtypes = [P, i32, i32, ctypes.POINTER(P)]
+        L.bs_kv_paged_reset.argtypes = [P]
+        L.bs_kv_paged_table.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(i32)]
+        L.bs_kv_paged_reorder.argtypes = [P, ctypes.POINTER(bs_kv_pool), i32]
+        L.bs_kv_paged_status.argtypes = [P, P, P]
+        L.bs_kv_paged_destroy.argtypes = [P]
+        L.bs_kv_paged_destroy.restype = None
         L.bs_verify_create.argtypes = [i32, i32, i32, i32, P, ctypes.POINTER(P)]
         L.bs_verify.argtypes = [P, P, i64, P, P, P]
         L.bs_verify_ex.argtypes = [P, P, i64, P, i32, i32, P, P, P]
@@ -83,6 +98,8 @@ def library() -> ctypes.CDLL:
         L.bs_verify_destroy.restype = None
         for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_finalize",
                      "bs_last_selection", "bs_get_finished", "bs_steps_taken",
+                     "bs_kv_paged_create", "bs_kv_paged_reset", "bs_kv_paged_table",
+                     "bs_kv_paged_reorder", "bs_kv_paged_status",
                      "bs_verify_create", "bs_verify", "bs_verify_ex"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -151,6 +168,51 @@ def make_kv_desc(planes: Sequence, pos_offset: int = 0) -> bs_kv_desc:
 
 def bs_reorder_kv(h: int, kv: bs_kv_desc, gen_len: int) -> None:
     _check(library().bs_reorder_kv(h, ctypes.byref(kv), gen_len), "bs_reorder_kv")
+
+
+def bs_kv_paged_create(h: int, block_size: int, blocks_per_item: int) -> int:
+    p = ctypes.c_void_p()
+    _check(library().bs_kv_paged_create(h, block_size, blocks_per_item, ctypes.byref(p)),
+           "bs_kv_paged_create")
+    return p.value
+
+
+def bs_kv_paged_reset(p: int) -> None:
+    _check(library().bs_kv_paged_reset(p), "bs_kv_paged_reset")
+
+
+def bs_kv_paged_table(p: int):
+    """(device address of the table, max_blocks)."""
+    t, mb = ctypes.c_void_p(), ctypes.c_int32()
+    _check(library().bs_kv_paged_table(p, ctypes.byref(t), ctypes.byref(mb)), "bs_kv_paged_table")
+    return t.value, mb.value
+
+
+def make_kv_pool(pools: Sequence) -> bs_kv_pool:
+    """Descriptor of block pools that are torch tensors [blocks, block_size, ...]."""
+    p0 = pools[0]
+    es = p0.element_size()
+    arr = (ctypes.c_void_p * len(pools))(*[p.data_ptr() for p in pools])
+    d = bs_kv_pool(len(pools), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                   p0.stride(0) * es, p0.stride(1) * es, p0[0, 0].numel() * es)
+    d._keep = arr  # the pointer array must outlive the call
+    return d
+
+
+def bs_kv_paged_reorder(p: int, pool: bs_kv_pool, gen_len: int) -> None:
+    _check(library().bs_kv_paged_reorder(p, ctypes.byref(pool), gen_len), "bs_kv_paged_reorder")
+
+
+def bs_kv_paged_status(p: int, batch: int):
+    """(overflow flag, free blocks per item as a list); synchronises."""
+    ov = ctypes.c_int32()
+    fb = (ctypes.c_int32 * batch)()
+    _check(library().bs_kv_paged_status(p, ctypes.byref(ov), fb), "bs_kv_paged_status")
+    return ov.value, list(fb)
+
+
+def bs_kv_paged_destroy(p: int) -> None:
+    library().bs_kv_paged_destroy(p)
 
 
 def bs_finalize(h: int, tokens, lengths, norm_scores) -> None:
@@ -304,6 +366,66 @@ class BeamSearch:
         nm = torch.empty((self.B, R), dtype=torch.float32, device=self.device)
         bs_finalize(self.h, tok, ln, nm)
         return tok, ln, nm
+
+
+class PagedKV:
+    """Block tables with copy on write for a BeamSearch's KV cache.
+
+    ``table()`` is the device table as a torch tensor [B*W, max_blocks]
+    (a view of the library's buffer); ``reorder(pools, t)`` follows the
+    bs_step of step t.
+    """
+
+    def __init__(self, search: "BeamSearch", block_size: int, blocks_per_item: int = 0):
+        self.search = search
+        self.block_size = block_size
+        mb = search.T // block_size + 1 if block_size >= 1 else 1
+        self.blocks_per_item = blocks_per_item or search.W * mb
+        self.h = bs_kv_paged_create(search.h, block_size, self.blocks_per_item)
+        self._addr, self.max_blocks = bs_kv_paged_table(self.h)
+
+    def table(self):
+        """A copy of the device table as a torch int32 tensor [B*W, max_blocks],
+        taken after the handle's stream has reached it."""
+        import torch
+        t = torch.empty((self.search.B * self.search.W, self.max_blocks), dtype=torch.int32,
+                        device=self.search.device)
+        torch.cuda.synchronize(self.search.device)
+        _hip_copy_d2d(t.data_ptr(), self._addr, t.numel() * 4)
+        return t
+
+    def reset(self):
+        bs_kv_paged_reset(self.h)
+
+    def reorder(self, pools_or_desc, gen_len: int):
+        d = pools_or_desc
+        if not isinstance(d, bs_kv_pool):
+            d = make_kv_pool(d)
+        bs_kv_paged_reorder(self.h, d, gen_len)
+
+    def status(self):
+        return bs_kv_paged_status(self.h, self.search.B)
+
+    def close(self):
+        if getattr(self, "h", None):
+            bs_kv_paged_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _hip_copy_d2d(dst: int, src: int, nbytes: int) -> None:
+    """Synchronous device-to-device copy through the HIP runtime torch loaded."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    rc = hip.hipMemcpy(dst, src, nbytes, 3)  # hipMemcpyDeviceToDevice
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
 
 
 class Verifier:

@@ -1472,6 +1472,220 @@ __global__ __launch_bounds__(64) void k5_finalize(K5Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// K6/K7: paged KV cache -- block tables with copy on write
+// ---------------------------------------------------------------------------
+
+constexpr int kPagedMaxBlocks = 4096;  // blocks per item (LDS reference counts)
+constexpr int kPagedMaxTable = 2048;   // W * max_blocks (LDS table copies)
+
+struct PagedDev {
+  int* table;     // [B*W][mb] global block ids, -1 = none
+  int* refc;      // [B*bpi] live-row references of each block
+  int* freel;     // [B][bpi] stack of free global block ids
+  int* nfree;     // [B]
+  int* overflow;  // [1]
+  int* cpy;       // [B*W][3] copy list of the step: source block, destination block, positions
+  int* ncpy;      // [2] entries of the list, by step parity
+};
+
+struct K6Args {
+  PagedDev pg;
+  const float* s;       // [B*W] running scores after the step
+  const uint8_t* done;  // [B] after the step
+  const int* plan;      // [B][kPlanStride] the step's reorder plan
+  int W, bs, bpi, mb, t;
+};
+
+// One workgroup per item. The item's table, reference counts and free list
+// are staged in LDS; the new table is formed from the old one and the plan,
+// references are added before old ones are dropped (a block both gains and
+// loses references without being freed in between), and a block whose count
+// reaches zero goes back to the free list. Then wave 0 makes position t
+// writable for every live slot.
+__global__ __launch_bounds__(kThreads) void k6_paged_reorder(K6Args a) {
+  __shared__ int refc[kPagedMaxBlocks];
+  __shared__ int fstack[kPagedMaxBlocks];
+  __shared__ int told[kPagedMaxTable];
+  __shared__ int tnew[kPagedMaxTable];
+  __shared__ int par[kMaxBeam];
+  __shared__ int nfree_sh;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int W = a.W, mb = a.mb, bpi = a.bpi, t = a.t, bs = a.bs;
+  const int base = b * bpi;          // the item's first global block id
+  const int nb = (t + bs - 1) / bs;  // blocks holding positions [0, t)
+  const int nt = W * mb;
+  const PagedDev& pg = a.pg;
+  const int* plan = a.plan + b * kPlanStride;
+  const bool item_done = a.done[b] != 0;
+  const int nf = min(max(pg.nfree[b], 0), bpi);
+  for (int e = tid; e < bpi; e += kThreads) refc[e] = pg.refc[base + e];
+  for (int e = tid; e < nf; e += kThreads) fstack[e] = pg.freel[base + e];
+  for (int e = tid; e < nt; e += kThreads) {
+    const int v = pg.table[(int64_t)b * nt + e];
+    told[e] = (v >= base && v < base + bpi) ? v : -1;  // only the item's own blocks
+  }
+  if (tid < W) {  // parent of each slot: itself unless the plan moves it
+    int pp = tid;
+    const int nsrc = plan[0];
+    if (plan[1] > 0)
+      for (int q = 0; q < nsrc; ++q)
+        if ((plan[2 + kMaxBeam + q] >> tid) & 1) pp = plan[2 + q];
+    par[tid] = pp;
+  }
+  if (tid == 0) nfree_sh = nf;
+  __syncthreads();
+
+  // new table: a live slot of a running item takes its parent's blocks
+  // [0, nb); rows of dead slots and of finished items hold nothing
+  for (int e = tid; e < nt; e += kThreads) {
+    const int i = e / mb, k = e - i * mb;
+    int v = -1;
+    if (!item_done && a.s[b * W + i] > -kInf && k < nb) v = told[par[i] * mb + k];
+    tnew[e] = v;
+  }
+  __syncthreads();
+  for (int e = tid; e < nt; e += kThreads)
+    if (tnew[e] >= 0) atomicAdd(&refc[tnew[e] - base], 1);
+  __syncthreads();
+  for (int e = tid; e < nt; e += kThreads)
+    if (told[e] >= 0 && atomicSub(&refc[told[e] - base], 1) == 1) {
+      const int slot = atomicAdd(&nfree_sh, 1);
+      if (slot < kPagedMaxBlocks) fstack[slot] = told[e];
+    }
+  __syncthreads();
+
+  // position t: a fresh block at a block boundary; inside a block that a
+  // lower live slot also holds, a private copy of its first t % bs positions
+  if (tid < 64) {
+    const int lane = tid;
+    const int blk = t / bs, off = t - blk * bs;
+    const bool live = lane < W && !item_done && a.s[b * W + lane] > -kInf;
+    const int cur = live ? tnew[lane * mb + blk] : -1;
+    bool shared = false;
+    for (int j = 0; j < W; ++j) {
+      const bool lj = !item_done && a.s[b * W + j] > -kInf;
+      if (j < lane && lj && cur >= 0 && tnew[j * mb + blk] == cur) shared = true;
+    }
+    const bool alloc = live && (off == 0 || cur < 0 || shared);
+    const bool copy = live && off > 0 && cur >= 0 && shared;
+    const uint64_t below = (lane == 0) ? 0 : (~(uint64_t)0 >> (64 - lane));
+    const uint64_t am = __ballot(alloc);
+    const int rank = __popcll(am & below);
+    const int avail = min(nfree_sh, bpi);
+    int nbk = -1;
+    if (alloc && rank < avail) nbk = fstack[avail - 1 - rank];
+    if (nbk < base || nbk >= base + bpi) nbk = -1;  // only the item's own blocks
+    const bool got = nbk >= 0;
+    if (alloc && !got) {  // out of blocks: the slot is left without one
+      pg.overflow[0] = 1;
+      if (cur >= 0) {
+        tnew[lane * mb + blk] = -1;
+        atomicSub(&refc[cur - base], 1);  // still held by a lower slot
+      }
+    }
+    const uint64_t cm = __ballot(copy && got);
+    // the item's copies go to the step's global list (one atomic per item);
+    // the other parity's count is cleared for the next step
+    int cbase = 0;
+    if (lane == 0 && cm) cbase = atomicAdd(&pg.ncpy[t & 1], __popcll(cm));
+    cbase = __builtin_amdgcn_readfirstlane(cbase);
+    if (b == 0 && lane == 0) pg.ncpy[(t + 1) & 1] = 0;
+    __builtin_amdgcn_wave_barrier();
+    if (got) {
+      tnew[lane * mb + blk] = nbk;
+      refc[nbk - base] = 1;
+      if (copy) {
+        atomicSub(&refc[cur - base], 1);
+        int* c = pg.cpy + ((int64_t)cbase + __popcll(cm & below)) * 3;
+        c[0] = cur;
+        c[1] = nbk;
+        c[2] = off;
+      }
+    }
+    if (lane == 0) {
+      const int used = __popcll(am) < avail ? __popcll(am) : avail;
+      nfree_sh = avail - used;
+    }
+  }
+  __syncthreads();
+
+  for (int e = tid; e < bpi; e += kThreads) pg.refc[base + e] = refc[e];
+  const int nf2 = min(nfree_sh, bpi);
+  for (int e = tid; e < nf2; e += kThreads) pg.freel[base + e] = fstack[e];
+  for (int e = tid; e < nt; e += kThreads) pg.table[(int64_t)b * nt + e] = tnew[e];
+  if (tid == 0) pg.nfree[b] = nf2;
+}
+
+struct K7Args {
+  char* pools[kMaxPlanesPerLaunch];
+  int n_planes;
+  int64_t block_stride, pos_stride;
+  int words_per_pos;
+  int tiles;             // word tiles of a copy of block_size - 1 positions
+  int groups;            // groups of kCopyPlanes pools
+  const int* cpy;
+  const int* ncpy;
+  int parity;
+  int max_copies;        // capacity of the list: B*W
+};
+
+// The copies on write of the step: a fixed grid walks the units (copy, word
+// tile, group of kCopyPlanes pools) of the step's list; a thread moves one
+// word of each pool of its unit's group, all loads issued before the first
+// store.
+constexpr int kCopyPlanes = 8;
+constexpr int kCopyGrid = 256;
+template <int WORD>
+__global__ __launch_bounds__(kThreads) void k7_paged_copy(K7Args a) {
+  using WT = typename Word<WORD>::type;
+  const int units = min(a.ncpy[a.parity], a.max_copies) * a.tiles * a.groups;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int f = u / (a.tiles * a.groups);
+    const int rest = u - f * a.tiles * a.groups;
+    const int tile = rest / a.groups, grp = rest - tile * a.groups;
+    const int* c = a.cpy + (int64_t)f * 3;
+    const int src = c[0], dst = c[1], npos = c[2];
+    const int e = tile * kThreads + threadIdx.x;
+    if (e >= npos * a.words_per_pos) continue;
+    const int pos = e / a.words_per_pos;
+    const int64_t off = pos * a.pos_stride + (int64_t)(e - pos * a.words_per_pos) * WORD;
+    const int64_t so = src * a.block_stride + off, d = dst * a.block_stride + off;
+    const int p0 = grp * kCopyPlanes;
+    const int np = min(kCopyPlanes, a.n_planes - p0);
+    WT v[kCopyPlanes];
+#pragma unroll
+    for (int k = 0; k < kCopyPlanes; ++k)
+      if (k < np) v[k] = *reinterpret_cast<const WT*>(a.pools[p0 + k] + so);
+#pragma unroll
+    for (int k = 0; k < kCopyPlanes; ++k)
+      if (k < np) *reinterpret_cast<WT*>(a.pools[p0 + k] + d) = v[k];
+  }
+}
+
+// Reset: row r of item b holds block b*bpi + w in logical block 0; the other
+// blocks of the item are free.
+__global__ void k6_paged_init(PagedDev pg, int B, int W, int bpi, int mb) {
+  const int b = blockIdx.x;
+  const int base = b * bpi;
+  for (int e = threadIdx.x; e < bpi; e += blockDim.x) {
+    pg.refc[base + e] = e < W ? 1 : 0;
+    if (e < bpi - W) pg.freel[base + e] = base + bpi - 1 - e;
+  }
+  for (int e = threadIdx.x; e < W * mb; e += blockDim.x) {
+    const int i = e / mb, k = e - i * mb;
+    pg.table[(int64_t)b * W * mb + e] = k == 0 ? base + i : -1;
+  }
+  if (threadIdx.x == 0) {
+    pg.nfree[b] = bpi - W;
+    if (b == 0) {
+      pg.overflow[0] = 0;
+      pg.ncpy[0] = 0;
+      pg.ncpy[1] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // init: running scores, finished sets, done flags, length-penalty table
 // ---------------------------------------------------------------------------
 
@@ -1521,6 +1735,14 @@ struct bs_state {
   float* ps;
   float* px;
   int* pv;
+};
+
+struct bs_kv_paged {
+  bs_state* h;
+  int bs, bpi, mb;
+  int last_t;  // the step last reordered (0: none since the reset)
+  void* block;
+  PagedDev pg;
 };
 
 struct bs_verify_state {
@@ -1895,6 +2117,163 @@ int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
     if (rc != BS_OK) return rc;
   }
   return BS_OK;
+}
+
+int bs_kv_paged_create(bs_state* h, int32_t block_size, int32_t blocks_per_item,
+                       bs_kv_paged** out) {
+  if (!h || !out) return BS_EINVAL;
+  *out = nullptr;
+  if (block_size < 1 || blocks_per_item < h->W || blocks_per_item > kPagedMaxBlocks)
+    return BS_EINVAL;
+  const int mb = h->T / block_size + 1;
+  if ((int64_t)h->W * mb > kPagedMaxTable) return BS_EINVAL;
+  if ((int64_t)h->B * blocks_per_item >= ((int64_t)1 << 31)) return BS_EINVAL;
+  bs_kv_paged* p = (bs_kv_paged*)calloc(1, sizeof(bs_kv_paged));
+  if (!p) return BS_ENOMEM;
+  p->h = h;
+  p->bs = block_size;
+  p->bpi = blocks_per_item;
+  p->mb = mb;
+  const size_t B = (size_t)h->B;
+  const size_t sizes[] = {
+      B * h->W * mb * 4,            // table
+      B * blocks_per_item * 4,      // reference counts
+      B * blocks_per_item * 4,      // free lists
+      B * 4,                        // free counts
+      4,                            // overflow flag
+      B * h->W * 3 * 4,             // the step's copy list
+      2 * 4,                        // its length, by step parity
+  };
+  const int n = sizeof(sizes) / sizeof(sizes[0]);
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += align_up(sizes[i]);
+  if (hipMalloc(&p->block, total) != hipSuccess) {
+    (void)hipGetLastError();
+    free(p);
+    return BS_ENOMEM;
+  }
+  char* q = (char*)p->block;
+  int* ptr[n];
+  for (int i = 0; i < n; ++i) {
+    ptr[i] = (int*)q;
+    q += align_up(sizes[i]);
+  }
+  p->pg.table = ptr[0];
+  p->pg.refc = ptr[1];
+  p->pg.freel = ptr[2];
+  p->pg.nfree = ptr[3];
+  p->pg.overflow = ptr[4];
+  p->pg.cpy = ptr[5];
+  p->pg.ncpy = ptr[6];
+  int rc = bs_kv_paged_reset(p);
+  if (rc == BS_OK && hipStreamSynchronize(h->stream) != hipSuccess) rc = BS_EDEVICE;
+  if (rc != BS_OK) {
+    (void)hipFree(p->block);
+    free(p);
+    return rc;
+  }
+  *out = p;
+  return BS_OK;
+}
+
+int bs_kv_paged_reset(bs_kv_paged* p) {
+  if (!p) return BS_EINVAL;
+  hipLaunchKernelGGL(k6_paged_init, dim3(p->h->B), dim3(kThreads), 0, p->h->stream, p->pg,
+                     p->h->B, p->h->W, p->bpi, p->mb);
+  const int rc = launch_status();
+  if (rc == BS_OK) p->last_t = 0;
+  return rc;
+}
+
+int bs_kv_paged_table(const bs_kv_paged* p, int32_t** table, int32_t* max_blocks) {
+  if (!p || !table || !max_blocks) return BS_EINVAL;
+  *table = p->pg.table;
+  *max_blocks = p->mb;
+  return BS_OK;
+}
+
+int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len) {
+  if (!p || !pool || !pool->pools || pool->n_planes < 1) return BS_EINVAL;
+  if (pool->block_stride <= 0 || pool->pos_stride <= 0 || pool->bytes_per_pos <= 0)
+    return BS_EINVAL;
+  if (pool->bytes_per_pos > pool->pos_stride ||
+      (int64_t)(p->bs - 1) * pool->pos_stride + pool->bytes_per_pos > pool->block_stride)
+    return BS_EINVAL;
+  bs_state* h = p->h;
+  // every step is reordered once, in order: the table of step t is built on
+  // that of step t-1
+  if (h->t == 0 || gen_len != h->t || p->last_t + 1 != h->t) return BS_ESTATE;
+  bool a16 = (pool->bytes_per_pos % 16 == 0) && (pool->pos_stride % 16 == 0) &&
+             (pool->block_stride % 16 == 0);
+  bool a4 = (pool->bytes_per_pos % 4 == 0) && (pool->pos_stride % 4 == 0) &&
+            (pool->block_stride % 4 == 0);
+  for (int i = 0; i < pool->n_planes; ++i) {
+    if (!pool->pools[i]) return BS_EINVAL;
+    a16 = a16 && ((uintptr_t)pool->pools[i] % 16 == 0);
+    a4 = a4 && ((uintptr_t)pool->pools[i] % 4 == 0);
+  }
+  if (!a4) return BS_EINVAL;
+  K6Args a6;
+  a6.pg = p->pg;
+  a6.s = h->st.s;
+  a6.done = h->st.done;
+  a6.plan = h->st.plan;
+  a6.W = h->W;
+  a6.bs = p->bs;
+  a6.bpi = p->bpi;
+  a6.mb = p->mb;
+  a6.t = gen_len;
+  hipLaunchKernelGGL(k6_paged_reorder, dim3(h->B), dim3(kThreads), 0, h->stream, a6);
+  int rc = launch_status();
+  if (rc != BS_OK) return rc;
+  const int word = a16 ? 16 : 4;
+  K7Args a7;
+  a7.block_stride = pool->block_stride;
+  a7.pos_stride = pool->pos_stride;
+  a7.words_per_pos = (int)(pool->bytes_per_pos / word);
+  a7.cpy = p->pg.cpy;
+  a7.ncpy = p->pg.ncpy;
+  a7.parity = gen_len & 1;
+  a7.max_copies = h->B * h->W;
+  const int64_t words = (int64_t)(p->bs - 1) * a7.words_per_pos;  // at most bs-1 positions
+  a7.tiles = (int)((words + kThreads - 1) / kThreads);
+  if (a7.tiles > 0) {
+    for (int p0 = 0; p0 < pool->n_planes; p0 += kMaxPlanesPerLaunch) {
+      const int np = pool->n_planes - p0 < kMaxPlanesPerLaunch ? pool->n_planes - p0
+                                                                : kMaxPlanesPerLaunch;
+      a7.n_planes = np;
+      a7.groups = (np + kCopyPlanes - 1) / kCopyPlanes;
+      for (int i = 0; i < np; ++i) a7.pools[i] = (char*)pool->pools[p0 + i];
+      if (word == 16)
+        hipLaunchKernelGGL(k7_paged_copy<16>, dim3(kCopyGrid), dim3(kThreads), 0, h->stream, a7);
+      else
+        hipLaunchKernelGGL(k7_paged_copy<4>, dim3(kCopyGrid), dim3(kThreads), 0, h->stream, a7);
+      rc = launch_status();
+      if (rc != BS_OK) return rc;
+    }
+  }
+  p->last_t = h->t;
+  return BS_OK;
+}
+
+int bs_kv_paged_status(bs_kv_paged* p, int32_t* overflow, int32_t* free_blocks) {
+  if (!p || !overflow) return BS_EINVAL;
+  hipStream_t s = p->h->stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return BS_EDEVICE;
+  if (hipMemcpy(overflow, p->pg.overflow, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return BS_EDEVICE;
+  if (free_blocks &&
+      hipMemcpy(free_blocks, p->pg.nfree, (size_t)p->h->B * 4, hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return BS_EDEVICE;
+  return BS_OK;
+}
+
+void bs_kv_paged_destroy(bs_kv_paged* p) {
+  if (!p) return;
+  (void)hipStreamSynchronize(p->h->stream);
+  (void)hipFree(p->block);
+  free(p);
 }
 
 int bs_finalize(bs_state* h, int32_t* tokens, int32_t* lengths, float* norm_scores) {

@@ -62,6 +62,10 @@ def parse():
                     help="verify: minimum accepted block size")
     ap.add_argument("--tile-elems", type=int, default=0, choices=[0, 16, 32, 64],
                     help="logits per thread in the streaming pass (0: the library's choice)")
+    ap.add_argument("--kv", default="contig", choices=["contig", "paged"],
+                    help="KV cache: contiguous rows (bs_reorder_kv) or block tables with copy "
+                         "on write (bs_kv_paged_reorder)")
+    ap.add_argument("--block-size", type=int, default=16, help="positions per block (--kv paged)")
     ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
     ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,11 +123,18 @@ def bench_search(args, torch, bs, dev):
         for i in range(s, pool_n, distinct_n):
             pool[i].copy_(src)
     gen_s = time.time() - t0
-    kv = [torch.zeros((wl.rows, T, bpp // 4), dtype=torch.int32, device=dev)
-          for _ in range(planes_n)]
-    desc = bs.make_kv_desc(kv, pos_offset=0)
-
     g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems)
+    paged = args.kv == "paged"
+    bsz = args.block_size
+    if paged:
+        pk = bs.PagedKV(g, bsz)
+        kv = [torch.zeros((B * pk.blocks_per_item, bsz, bpp // 4), dtype=torch.int32, device=dev)
+              for _ in range(planes_n)]
+        desc = bs.make_kv_pool(kv)
+    else:
+        kv = [torch.zeros((wl.rows, T, bpp // 4), dtype=torch.int32, device=dev)
+              for _ in range(planes_n)]
+        desc = bs.make_kv_desc(kv, pos_offset=0)
     n_hist = args.steps
     hist_bi = torch.empty((n_hist, B, W), dtype=torch.int32, device=dev)
     hist_tk = torch.empty_like(hist_bi)
@@ -137,26 +148,34 @@ def bench_search(args, torch, bs, dev):
               for _ in range(args.steps if args.events else 0)]
     hist = [(hist_bi[i], hist_tk[i], hist_sc[i], hist_dn[i]) for i in range(n_hist)]
 
+    def reset():
+        g.reset()
+        if paged:
+            pk.reset()
+
     def run(n, record):
         ts = []
         for i in range(n):
             t = (g.steps % T) + 1
             if t == 1 and g.steps:
-                g.reset()
+                reset()
             o = hist[i] if record else hist[0]
             bs.bs_step(g.h, pool[(t - 1) % pool_n], *o)
             if record and args.events:
                 events[i][0].record(stream)
-            bs.bs_reorder_kv(g.h, desc, t)
+            if paged:
+                bs.bs_kv_paged_reorder(pk.h, desc, t)
+            else:
+                bs.bs_reorder_kv(g.h, desc, t)
             if record and args.events:
                 events[i][1].record(stream)
             ts.append(t)
         return ts
 
     # warmup (untimed), then the timed region
-    g.reset()
+    reset()
     run(args.warmup, False)
-    g.reset()
+    reset()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ts = run(args.steps, True)
@@ -176,15 +195,29 @@ def bench_search(args, torch, bs, dev):
             prev_live[:, 0] = True
         live_rows = int(prev_live.sum())                  # rows the step had to read
         logit_bytes.append(live_rows * V * wl.elem_bytes + 20 * B * W)
-        moved_total = 0
-        for b in range(B):
-            if dn[i, b]:
-                continue
-            live = sc[i, b] > -np.inf
-            moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
-            parents = {int(bi[i, b, w]) for w in moved}
-            moved_total += len(moved) + len(parents)
-        kv_bytes.append(moved_total * t * bpp * planes_n)
+        if paged:
+            # copies on write: live slots beyond the first of each parent,
+            # t % block_size positions each, read and written in every pool;
+            # plus the items' tables, reference counts and free lists
+            copies = 0
+            if t % bsz:
+                for b in range(B):
+                    if dn[i, b]:
+                        continue
+                    lv = [w for w in range(W) if sc[i, b, w] > -np.inf]
+                    copies += len(lv) - len({int(bi[i, b, w]) for w in lv})
+            kv_bytes.append(2 * copies * (t % bsz) * bpp * planes_n
+                            + 2 * B * (W * pk.max_blocks + 2 * pk.blocks_per_item) * 4)
+        else:
+            moved_total = 0
+            for b in range(B):
+                if dn[i, b]:
+                    continue
+                live = sc[i, b] > -np.inf
+                moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
+                parents = {int(bi[i, b, w]) for w in moved}
+                moved_total += len(moved) + len(parents)
+            kv_bytes.append(moved_total * t * bpp * planes_n)
         prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
     kv_bytes = np.array(kv_bytes, np.float64)
     logit_bytes = np.array(logit_bytes, np.float64)
@@ -205,10 +238,12 @@ def bench_search(args, torch, bs, dev):
         "config": {
             "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
                         f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
-                        f"gen_len = t" + (", 2W-candidate fill" if args.prune == "top2w" else ""),
+                        f"gen_len = t" + (", 2W-candidate fill" if args.prune == "top2w" else "")
+                        + (f", paged KV (blocks of {bsz} positions, copy on write)" if paged else ""),
             "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype, "prune": args.prune,
             "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
-            "logit_pool_buffers": pool_n,
+            "logit_pool_buffers": pool_n, "kv": args.kv,
+            **({"block_size": bsz} if paged else {}),
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
         "live_item_steps": int((~dn).sum()),
@@ -220,20 +255,38 @@ def bench_search(args, torch, bs, dev):
         d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
                            for i in range(1, len(events))]) * 1e-3
         ach = kv_bytes.sum() / d_kv.sum() / 1e9
-        out["roofline"] = {
-            "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-            "traffic": measured_traffic(wl.name),
-            "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
-        }
+        step_gbs = logit_bytes[1:].sum() / d_step.sum() / 1e9
+        if paged:
+            # the logits pass dominates once the reorder moves only partial blocks
+            out["roofline"] = {
+                "bound": "hbm", "kernel": "k1_expand_select + k2_select_finalize",
+                "achieved": step_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": step_gbs / PEAK_HBM_GBS, "traffic": None,
+                "alg_bytes_per_launch": logit_bytes.mean(), "avg_launch_us": 1e6 * d_step.mean(),
+            }
+            out["paged_reorder"] = {
+                "kernels": "k6_paged_reorder + k7_paged_copy", "avg_us": 1e6 * d_kv.mean(),
+                "alg_bytes_per_step": kv_bytes.mean(), "alg_gbs": ach,
+            }
+        else:
+            out["roofline"] = {
+                "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": measured_traffic(wl.name),
+                "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
+            }
         out["step_kernels"] = {
-            "kernels": "k1_expand_select + k2_merge_finalize (event gap between reorders)",
+            "kernels": "k1_expand_select + k2 (event gap between reorders)",
             "avg_us": 1e6 * d_step.mean(),
-            "alg_gbs": logit_bytes[1:].sum() / d_step.sum() / 1e9,
+            "alg_gbs": step_gbs,
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
+    if paged:
+        ov, _ = pk.status()
+        out["paged_overflow"] = bool(ov)
+        pk.close()
     g.close()
     return out
 

@@ -174,6 +174,85 @@ typedef struct {
  * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
 int bs_reorder_kv(bs_state *h, const bs_kv_desc *kv, int32_t gen_len);
 
+/* Paged KV cache ("llm_internals" 9.2.2, KV-cache paragraph: with a paged
+ * cache the reorder becomes a rewrite of block-table entries, and a block is
+ * copied only when a shared block is about to be written, i.e. copy on
+ * write; 9.2.4: the generated parts' common prefixes are then shared too).
+ *
+ * The generated positions of every row live in blocks of block_size
+ * positions in block pools owned by the caller, one pool per layer and K or
+ * V, all indexed by the same block ids. Row r = b*W+w maps its logical block
+ * k (positions k*block_size .. (k+1)*block_size-1) to the physical block
+ * table[r][k], or -1 for none. Item b owns the physical blocks
+ * [b*blocks_per_item, (b+1)*blocks_per_item): rows share blocks only within
+ * an item, and a block shared by two live rows is never written. The handle
+ * owns the table, the reference counts and each item's free list. */
+typedef struct bs_kv_paged bs_kv_paged;
+
+/* Every pool holds B * blocks_per_item blocks of block_size positions. */
+typedef struct {
+    int32_t n_planes;        /* >= 1                                          */
+    void *const *pools;      /* host array of n_planes device pointers        */
+    int64_t block_stride;    /* bytes between physical block k and k+1        */
+    int64_t pos_stride;      /* bytes between positions p and p+1 of a block  */
+    int64_t bytes_per_pos;   /* bytes of one position of one row              */
+} bs_kv_pool;
+
+/* Creates the paged tables for handle h (B items, W beams, T = max_steps):
+ * the table [B*W][max_blocks] with max_blocks = T / block_size + 1 (blocks
+ * for positions 0..T), and per item blocks_per_item reference counts and a
+ * free list. Then resets them as bs_kv_paged_reset does. Synchronises.
+ *   block_size       positions per block, >= 1
+ *   blocks_per_item  W <= blocks_per_item <= 4096; W * max_blocks always
+ *                    suffices, fewer relies on shared prefixes
+ * Limit: W * max_blocks <= 2048.
+ * Errors: BS_EINVAL; BS_ENOMEM; BS_EDEVICE. */
+int bs_kv_paged_create(bs_state *h, int32_t block_size, int32_t blocks_per_item,
+                       bs_kv_paged **out);
+
+/* Every row gets a private block for its logical block 0, so position 0 of
+ * every row is writable; every other block of the item is free. Call it
+ * together with bs_reset, before the first bs_step of a search. */
+int bs_kv_paged_reset(bs_kv_paged *p);
+
+/* The device table, int32 [B*W][max_blocks] (row r at table + r*max_blocks),
+ * valid until bs_kv_paged_destroy; the caller reads it to address the pools
+ * and must not write it. */
+int bs_kv_paged_table(const bs_kv_paged *p, int32_t **table, int32_t *max_blocks);
+
+/* The reorder that follows the bs_step of step t, with gen_len = t positions
+ * [0, t) written:
+ *  (1) for every live slot i of an item not done after the step whose parent
+ *      p = beam_idx[b][i] differs from i, row i's blocks 0..ceil(t/block_size)-1
+ *      become row p's (block ids are copied, not data); blocks no live row of
+ *      an item still running references any more (those of overwritten rows,
+ *      of dead slots and of items that are done) return to the free list;
+ *  (2) position t is made writable for every live slot of an item not done:
+ *      at a block boundary (t % block_size == 0) the slot gets a fresh block;
+ *      otherwise, where live slots share the block holding position t, every
+ *      slot but the lowest gets a private copy of that block's first
+ *      t % block_size positions in every pool (the copy on write).
+ * Afterwards every live row's positions [0, t), read through the table, hold
+ * what its parent's held before the call, bit for bit.
+ *   pool     host descriptor of the caller's pools; block_stride, pos_stride,
+ *            bytes_per_pos and every pool address must be multiples of 4 bytes
+ *            (16 for the fast path)
+ *   gen_len  must equal the steps taken: one call after every bs_step, in
+ *            order, starting at step 1 after bs_kv_paged_reset
+ * An item that runs out of free blocks leaves the slot's entry at -1 and sets
+ * the overflow flag read by bs_kv_paged_status.
+ * Errors: BS_EINVAL; BS_ESTATE (gen_len is not the steps taken, or the
+ * previous step was not reordered, or this one already was); BS_EDEVICE. */
+int bs_kv_paged_reorder(bs_kv_paged *p, const bs_kv_pool *pool, int32_t gen_len);
+
+/* Synchronises the handle's stream, then reports whether any item ran out of
+ * free blocks since the last reset (*overflow, host int32) and, when
+ * free_blocks is not NULL, each item's free block count (host int32 [B]). */
+int bs_kv_paged_status(bs_kv_paged *p, int32_t *overflow, int32_t *free_blocks);
+
+/* Frees the tables after synchronising the stream. */
+void bs_kv_paged_destroy(bs_kv_paged *p);
+
 /* Final selection (batched section of "Transformers中的Beam Search高效实现",
  * after the decode loop): every live beam of an item that is not done joins
  * a copy of its finished set with |y| = steps taken; the best num_return

@@ -11,7 +11,7 @@ import beam_search_step_amd as bs
 
 def test_library_exports_every_declared_function():
     names = bs.declared_functions()
-    assert len(names) == 14
+    assert len(names) == 20
     lib = bs.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, f"not exported: {missing}"
@@ -67,8 +67,14 @@ def test_null_arguments_are_rejected():
     h = ctypes.c_void_p()
     assert L.bs_verify_create(0, 8, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
     assert L.bs_verify_create(2, 65, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
+    assert L.bs_kv_paged_create(None, 16, 64, ctypes.byref(h)) == bs.BS_EINVAL
+    assert L.bs_kv_paged_reset(None) == bs.BS_EINVAL
+    assert L.bs_kv_paged_table(None, None, None) == bs.BS_EINVAL
+    assert L.bs_kv_paged_reorder(None, None, 1) == bs.BS_EINVAL
+    assert L.bs_kv_paged_status(None, None, None) == bs.BS_EINVAL
     L.bs_destroy(None)
     L.bs_verify_destroy(None)
+    L.bs_kv_paged_destroy(None)
 
 
 def test_config_struct_layout_matches_header():
@@ -78,3 +84,6 @@ def test_config_struct_layout_matches_header():
     assert bs.bs_config.tile_elems.offset == 48
     assert bs.bs_config.prune.offset == 52
     assert ctypes.sizeof(bs.bs_kv_desc) == 48
+    # int32 then a pointer (8-aligned), then three int64
+    assert ctypes.sizeof(bs.bs_kv_pool) == 40
+    assert bs.bs_kv_pool.block_stride.offset == 16
