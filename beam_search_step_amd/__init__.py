@@ -22,11 +22,13 @@ BS_F32, BS_BF16 = 0, 1
 BS_LP_NONE, BS_LP_GNMT, BS_LP_POW = 0, 1, 2
 BS_STOP_TRUE, BS_STOP_HEURISTIC, BS_STOP_NEVER = 0, 1, 2
 BS_PRUNE_TOPW, BS_PRUNE_TOP2W = 0, 1
+BS_SELECT_FUSED, BS_SELECT_TWO_PASS = 0, 1
 
 DTYPES = {"f32": BS_F32, "bf16": BS_BF16}
 LPS = {"none": BS_LP_NONE, "gnmt": BS_LP_GNMT, "pow": BS_LP_POW}
 STOPS = {"true": BS_STOP_TRUE, "heuristic": BS_STOP_HEURISTIC, "never": BS_STOP_NEVER}
 PRUNES = {"topw": BS_PRUNE_TOPW, "top2w": BS_PRUNE_TOP2W}
+SELECTS = {"fused": BS_SELECT_FUSED, "two_pass": BS_SELECT_TWO_PASS}
 
 
 class bs_config(ctypes.Structure):
@@ -35,7 +37,7 @@ class bs_config(ctypes.Structure):
         ("max_steps", ctypes.c_int32), ("eos_id", ctypes.c_int32), ("pad_id", ctypes.c_int32),
         ("logits_dtype", ctypes.c_int32), ("lp", ctypes.c_int32), ("alpha", ctypes.c_double),
         ("stop", ctypes.c_int32), ("num_return", ctypes.c_int32), ("tile_elems", ctypes.c_int32),
-        ("prune", ctypes.c_int32),
+        ("prune", ctypes.c_int32), ("select", ctypes.c_int32),
     ]
 
 
@@ -287,14 +289,14 @@ class BeamSearch:
 
     def __init__(self, batch, beam, vocab, max_steps, eos_id=-1, pad_id=-1, dtype="f32",
                  lp="gnmt", alpha=0.6, stop="heuristic", num_return=1, tile_elems=0,
-                 prune="topw", stream=None):
+                 prune="topw", select="fused", stream=None):
         import torch
         self.B, self.W, self.V, self.T = batch, beam, vocab, max_steps
         self.K = 2 * beam if prune == "top2w" else beam   # candidates ranked per item
         self.num_return = num_return
         self.cfg = bs_config(batch, beam, vocab, max_steps, eos_id, pad_id, DTYPES[dtype],
                              LPS[lp], float(alpha), STOPS[stop], num_return, tile_elems,
-                             PRUNES[prune])
+                             PRUNES[prune], SELECTS[select])
         self.stream = stream
         self.h = bs_create(self.cfg, stream)
         dev = torch.device("cuda", torch.cuda.current_device())

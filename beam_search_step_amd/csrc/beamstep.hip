@@ -1131,6 +1131,293 @@ __global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// L1-L3: the two-pass (coarse-to-fine) selection of the LightSeq article
+// ("层级式解码计算"), a measured alternative to K1/K2
+// ---------------------------------------------------------------------------
+
+struct CFArgs {
+  const void* logits;
+  int64_t stride;       // elements between rows
+  int V, W, K, KP;      // KP: groups per row, a power of two >= K (<= 16)
+  int tile, tiles;
+  const float* s;       // [B*W] running scores
+  const uint8_t* done;  // [B]
+  float* pm;            // [rows][tiles] tile maximum
+  float* ps;            // [rows][tiles] sum of exp(x - tile maximum)
+  float* gm;            // [rows][tiles][KP] the tile's group maxima
+  float* qc;            // [B][cap] queued candidate scores
+  int* qj;              // [B][cap] their flat indices
+  int* qn;              // [B] queue lengths (a length above cap: overflow)
+  int cap;
+};
+
+// The row state and the tile, requested together (as in K1).
+template <typename T, int EPT, bool ALIGNED>
+__device__ __forceinline__ bool cf_load(const CFArgs& a, int r, int v0, int vend,
+                                        float (&x)[EPT], float& sr) {
+  const int b = r / a.W;
+  const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
+  const uint32_t done_word = reinterpret_cast<const uint32_t*>(a.done)[b >> 2];
+  sr = a.s[r];
+  __asm__ volatile("" ::: "memory");
+  load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
+  return ((done_word >> (8 * (b & 3))) & 0xff) == 0 && sr > -kInf;
+}
+
+// L1, grid (tiles, rows): the tile's (max, sum exp) and the maxima of its KP
+// groups (lane mod KP: every group of the row takes elements from every tile).
+template <typename T, int EPT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void l1_coarse(CFArgs a) {
+  __shared__ float wm[kWaves], ws[kWaves];
+  __shared__ float wg[kWaves][kMaxBeam];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int v0 = c * a.tile, vend = min(a.V, v0 + a.tile);
+  float x[EPT], sr;
+  if (!cf_load<T, EPT, ALIGNED>(a, r, v0, vend, x, sr)) return;
+  float m = -kInf;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) m = fmaxf(m, x[i]);
+  float g = m;  // lanes l and l ^ st share l mod KP for st >= KP
+  for (int st = a.KP; st < 64; st <<= 1) g = fmaxf(g, __shfl_xor(g, st));
+  if (lane < a.KP) wg[wave][lane] = g;
+  const float mw = wave_max_f(m);
+  float sum = 0.0f;
+  if (mw > -kInf) {
+    const float off = -mw * kLog2e;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, off));
+  }
+  sum = wave_sum_f(sum);
+  if (lane == 0) {
+    wm[wave] = mw;
+    ws[wave] = sum;
+  }
+  __syncthreads();
+  const int64_t pt = (int64_t)r * a.tiles + c;
+  if (tid == 0) {
+    float M = wm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
+    float S = 0.0f;
+    if (M > -kInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (wm[w] > -kInf) S += ws[w] * exp2f((wm[w] - M) * kLog2e);
+    }
+    a.pm[pt] = M;
+    a.ps[pt] = S;
+  }
+  if (tid < a.KP)
+    a.gm[pt * a.KP + tid] = fmaxf(fmaxf(wg[0][tid], wg[1][tid]), fmaxf(wg[2][tid], wg[3][tid]));
+}
+
+// L2, grid (tiles, rows): the row's lse and threshold R (the K-th largest of
+// its KP group maxima: KP distinct elements, so R is at most the row's K-th
+// best logit), then the second read of the tile queues every logit >= R with
+// its candidate score fp32(s + fp32(x - lse)), one queue slot range per wave
+// (one device-scope atomic).
+template <typename T, int EPT, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void l2_fine(CFArgs a) {
+  __shared__ float sh_R, sh_lse;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, c = blockIdx.x, b = r / a.W, w = r - b * a.W;
+  const int v0 = c * a.tile, vend = min(a.V, v0 + a.tile);
+  float x[EPT], sr;
+  if (!cf_load<T, EPT, ALIGNED>(a, r, v0, vend, x, sr)) return;
+  if (wave == 0) {
+    const int64_t p0 = (int64_t)r * a.tiles;
+    float M = -kInf;
+    for (int t = lane; t < a.tiles; t += 64) M = fmaxf(M, a.pm[p0 + t]);
+    M = wave_max_f(M);
+    float S = 0.0f;
+    if (M > -kInf)
+      for (int t = lane; t < a.tiles; t += 64) {
+        const float mt = a.pm[p0 + t];
+        if (mt > -kInf) S += a.ps[p0 + t] * exp2f((mt - M) * kLog2e);
+      }
+    S = wave_sum_f(S);
+    float gv = -kInf;
+    if (lane < a.KP)
+      for (int t = 0; t < a.tiles; ++t) gv = fmaxf(gv, a.gm[(p0 + t) * a.KP + lane]);
+    int gt = 0, ge = 0;
+    for (int q = 0; q < a.KP; ++q) {
+      const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), q));
+      gt += o > gv ? 1 : 0;
+      ge += o >= gv ? 1 : 0;
+    }
+    // the K-th largest: at most K-1 larger and at least K not smaller (self included)
+    const uint64_t hit = __ballot(lane < a.KP && gt <= a.K - 1 && ge >= a.K);
+    const int hl = hit ? __builtin_ctzll(hit) : 0;
+    const float R = hit ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), hl))
+                        : -kInf;
+    if (lane == 0) {
+      sh_R = R;
+      sh_lse = M > -kInf ? M + logf(S) : -kInf;
+    }
+  }
+  __syncthreads();
+  float R = sh_R;
+  const float lse = sh_lse;
+  if (!(lse > -kInf)) return;
+  if (!(R > -kInf)) R = -3.402823466e38f;  // -inf is never a candidate
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) n += __popcll(__ballot(x[i] >= R));
+  if (n == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&a.qn[b], n);
+  base = __builtin_amdgcn_readfirstlane(base);
+  float* qc = a.qc + (int64_t)b * a.cap;
+  int* qj = a.qj + (int64_t)b * a.cap;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const bool cand = x[i] >= R;
+    const uint64_t bm = __ballot(cand);
+    if (bm) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                 (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0));
+      if (cand && pos < a.cap) {
+        const float logp = x[i] - lse;
+        qc[pos] = sr + logp;
+        qj[pos] = w * a.V + TileMap<T, ALIGNED>::col(v0, i);
+      }
+      base += __popcll(bm);
+    }
+  }
+}
+
+// The best K keys of an item over per-thread key arrays: K rounds of a
+// workgroup maximum over the keys below the previous round's winner.
+// out[r] (LDS) gets round r's key (0: none). Call with every thread.
+template <int N>
+__device__ __forceinline__ void block_topk(const uint64_t (&k)[N], int K, uint64_t* wbest,
+                                           uint64_t* out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t prev = ~(uint64_t)0;
+  for (int r = 0; r < K; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int q = 0; q < N; ++q) best = (k[q] < prev && k[q] > best) ? k[q] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) wbest[wave] = best;
+    __syncthreads();
+    uint64_t m = wbest[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = wbest[w] > m ? wbest[w] : m;
+    if (threadIdx.x == 0) out[r] = m;
+    __syncthreads();
+    prev = m;
+  }
+}
+
+struct L3Args {
+  K2Args k2;
+  CFArgs cf;
+};
+
+// L3, one workgroup per item: the K best queued candidates, exactly ordered by
+// (score desc, flat index asc), then the finalize of K2. A queue that
+// overflowed (massive ties above R) falls back to an exact scan of the item's
+// logits: K rounds of a workgroup maximum over all W*V candidates.
+template <int WMAX, typename T>
+__global__ __launch_bounds__(kThreads) void l3_sort_finalize(L3Args args) {
+  constexpr int kPer = kMaxBeam;  // queue entries per thread: cap = 256 * KP <= 256 * 16
+  __shared__ HypSmem<WMAX> hy;
+  __shared__ uint64_t wbest[kWaves];
+  __shared__ uint64_t best[WMAX];
+  __shared__ float lse_sh[kMaxBeam];
+  __shared__ int plan[kPlanStride];
+  const K2Args& a = args.k2;
+  const CFArgs& cf = args.cf;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = a.W, K = a.K, V = a.V;
+  const DevState& st = a.st;
+  if (tid < W) {
+    const int e = b * W + tid;
+    hy.norm[tid] = st.hnorm[e];
+    hy.raw[tid] = st.hraw[e];
+    hy.len[tid] = st.hlen[e];
+    hy.step[tid] = st.hstep[e];
+    hy.rank[tid] = st.hrank[e];
+    hy.par[tid] = st.hpar[e];
+    hy.tok[tid] = st.htok[e];
+  }
+  if (tid == 0) hy.count = st.hcount[b];
+  const int done = st.done[b];
+  const double lp_t = st.lpt[a.t], lp_T = st.lpt[a.T];
+  const int n = cf.qn[b];
+  __syncthreads();
+  if (tid == 0) cf.qn[b] = 0;  // the queue is empty for the next step
+  if (done) {
+    noop_item(a, b, tid);
+    return;
+  }
+  if (n <= cf.cap) {
+    uint64_t k[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = q * kThreads + tid;
+      k[q] = 0;
+      if (e < n) k[q] = pack_key(cf.qc[(int64_t)b * cf.cap + e], cf.qj[(int64_t)b * cf.cap + e]);
+    }
+    block_topk<kPer>(k, K, wbest, best);
+  } else {
+    // exact fallback: the lse of each live row, then K rounds over all of the
+    // item's candidates
+    if (wave == 0) {
+      for (int w = 0; w < W; ++w) {
+        const int64_t p0 = (int64_t)(b * W + w) * cf.tiles;
+        float M = -kInf;
+        for (int t = lane; t < cf.tiles; t += 64) M = fmaxf(M, cf.pm[p0 + t]);
+        M = wave_max_f(M);
+        float S = 0.0f;
+        if (M > -kInf)
+          for (int t = lane; t < cf.tiles; t += 64) {
+            const float mt = cf.pm[p0 + t];
+            if (mt > -kInf) S += cf.ps[p0 + t] * exp2f((mt - M) * kLog2e);
+          }
+        S = wave_sum_f(S);
+        if (lane == 0)
+          lse_sh[w] = (st.s[b * W + w] > -kInf && M > -kInf) ? M + logf(S) : -kInf;
+      }
+    }
+    __syncthreads();
+    uint64_t prev = ~(uint64_t)0;
+    for (int r = 0; r < K; ++r) {
+      uint64_t bk = 0;
+      for (int w = 0; w < W; ++w) {
+        const float lw = lse_sh[w];
+        if (!(lw > -kInf)) continue;
+        const float sw = st.s[b * W + w];
+        const T* row = reinterpret_cast<const T*>(cf.logits) + (int64_t)(b * W + w) * cf.stride;
+        for (int v = tid; v < V; v += kThreads) {
+          const float xv = Elem<T>::load1(row + v);
+          if (!(xv > -kInf)) continue;
+          const float logp = xv - lw;
+          const float cv = sw + logp;
+          if (!(cv > -kInf)) continue;
+          const uint64_t kk = pack_key(cv, w * V + v);
+          bk = (kk < prev && kk > bk) ? kk : bk;
+        }
+      }
+      bk = wave_max_u64(bk);
+      if (lane == 0) wbest[wave] = bk;
+      __syncthreads();
+      uint64_t m = wbest[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = wbest[w] > m ? wbest[w] : m;
+      if (tid == 0) best[r] = m;
+      __syncthreads();
+      prev = m;
+    }
+  }
+  if (wave != 0) return;
+  const uint64_t key = lane < K ? best[lane] : 0;
+  finalize_item<WMAX>(a, hy, plan, b, lane, key, lp_t, lp_T);
+}
+
+// ---------------------------------------------------------------------------
 // K3: in-place KV reorder
 // ---------------------------------------------------------------------------
 
@@ -1692,6 +1979,7 @@ __global__ void k6_paged_init(PagedDev pg, int B, int W, int bpi, int mb) {
 struct InitArgs {
   DevState st;
   double* lpt;
+  int* qn;  // two-pass queue lengths, or null
   int B, W, T, lp;
   double alpha;
 };
@@ -1706,6 +1994,7 @@ __global__ void k0_init(InitArgs a) {
     a.st.done[i] = 0;
     a.st.hcount[i] = 0;
     a.st.plan[i * kPlanStride + 1] = 0;
+    if (a.qn) a.qn[i] = 0;
   }
   if (i <= a.T) {
     double v = 1.0;
@@ -1735,6 +2024,12 @@ struct bs_state {
   float* ps;
   float* px;
   int* pv;
+  // two-pass selection
+  int KP, cap;
+  float* gm;
+  float* qc;
+  int* qj;
+  int* qn;
 };
 
 struct bs_kv_paged {
@@ -1804,6 +2099,34 @@ void launch_k1(const K1Args& a, int wmax, int dtype, int ept, bool aligned, dim3
     case 4: launch_k1_t<4>(a, dtype, ept, aligned, grid, s); break;
     case 8: launch_k1_t<8>(a, dtype, ept, aligned, grid, s); break;
     default: launch_k1_t<16>(a, dtype, ept, aligned, grid, s); break;
+  }
+}
+
+template <typename T, int EPT>
+void launch_cf_a(const CFArgs& a, bool aligned, dim3 grid, hipStream_t s) {
+  if (aligned) {
+    hipLaunchKernelGGL((l1_coarse<T, EPT, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((l2_fine<T, EPT, true>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((l1_coarse<T, EPT, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((l2_fine<T, EPT, false>), grid, dim3(kThreads), 0, s, a);
+  }
+}
+template <typename T>
+void launch_cf_t(const CFArgs& a, int ept, bool aligned, dim3 grid, hipStream_t s) {
+  if (ept == 64) launch_cf_a<T, 64>(a, aligned, grid, s);
+  else if (ept == 32) launch_cf_a<T, 32>(a, aligned, grid, s);
+  else launch_cf_a<T, 16>(a, aligned, grid, s);
+}
+template <typename T>
+void launch_l3_t(const L3Args& a, int wmax, hipStream_t s) {
+  dim3 g(a.k2.B), blk(kThreads);
+  switch (wmax) {
+    case 1: hipLaunchKernelGGL((l3_sort_finalize<1, T>), g, blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((l3_sort_finalize<2, T>), g, blk, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((l3_sort_finalize<4, T>), g, blk, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((l3_sort_finalize<8, T>), g, blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((l3_sort_finalize<16, T>), g, blk, 0, s, a); break;
   }
 }
 
@@ -1885,10 +2208,35 @@ void launch_k4_a(const K4Args& a, bool aligned, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((k4_verify<T, EPT, false, COUNT>), grid, dim3(kThreads), 0, s, a);
 }
 
+void fill_k2_args(K2Args& a2, bs_state* h, int t, int32_t* beam_idx, int32_t* token_id,
+                  float* scores, uint8_t* done) {
+  a2.st = h->st;
+  a2.pm = h->pm;
+  a2.ps = h->ps;
+  a2.px = h->px;
+  a2.pv = h->pv;
+  a2.B = h->B;
+  a2.W = h->W;
+  a2.K = h->K;
+  a2.V = h->V;
+  a2.T = h->T;
+  a2.tiles = h->tiles;
+  a2.eos = h->cfg.eos_id;
+  a2.pad = h->cfg.pad_id;
+  a2.stop = h->cfg.stop;
+  a2.alpha = h->cfg.alpha;
+  a2.t = t;
+  a2.out_beam = beam_idx;
+  a2.out_tok = token_id;
+  a2.out_score = scores;
+  a2.out_done = done;
+}
+
 int launch_init(bs_state* h) {
   InitArgs ia;
   ia.st = h->st;
   ia.lpt = h->lpt;
+  ia.qn = h->qn;
   ia.B = h->B;
   ia.W = h->W;
   ia.T = h->T;
@@ -1932,6 +2280,7 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   if (!(c.alpha == c.alpha)) return BS_EINVAL;
   if (c.prune != BS_PRUNE_TOPW && c.prune != BS_PRUNE_TOP2W) return BS_EINVAL;
   if (c.prune == BS_PRUNE_TOP2W && 2 * c.beam > kMaxBeam) return BS_EINVAL;
+  if (c.select != BS_SELECT_FUSED && c.select != BS_SELECT_TWO_PASS) return BS_EINVAL;
 
   bs_state* h = (bs_state*)calloc(1, sizeof(bs_state));
   if (!h) return BS_ENOMEM;
@@ -1956,6 +2305,9 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   const size_t RW = (size_t)h->rows;
   const size_t PT = RW * h->tiles;
   const size_t BT = (size_t)h->T * RW;
+  const bool two = c.select == BS_SELECT_TWO_PASS;
+  h->KP = pow2ceil(h->K);
+  h->cap = kThreads * h->KP;
   size_t sizes[] = {
       RW * 4,                 // s
       RW * 4,                 // slot_rank
@@ -1968,6 +2320,9 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
       ((size_t)h->T + 1) * 8, // lpt
       PT * 4, PT * 4,         // pm, ps
       PT * h->kmax * 4, PT * h->kmax * 4,  // px, pv
+      two ? PT * h->KP * 4 : 0,            // two-pass: group maxima
+      two ? (size_t)h->B * h->cap * 4 : 0, two ? (size_t)h->B * h->cap * 4 : 0,  // queue
+      two ? (size_t)h->B * 4 : 0,          // queue lengths
   };
   const int n = sizeof(sizes) / sizeof(sizes[0]);
   size_t total = 0;
@@ -2006,6 +2361,14 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   h->ps = (float*)ptr[i++];
   h->px = (float*)ptr[i++];
   h->pv = (int*)ptr[i++];
+  h->gm = two ? (float*)ptr[i] : nullptr;
+  ++i;
+  h->qc = two ? (float*)ptr[i] : nullptr;
+  ++i;
+  h->qj = two ? (int*)ptr[i] : nullptr;
+  ++i;
+  h->qn = two ? (int*)ptr[i] : nullptr;
+  ++i;
 
   int rc = launch_init(h);
   if (rc == BS_OK && hipStreamSynchronize(h->stream) != hipSuccess) rc = BS_EDEVICE;
@@ -2034,6 +2397,41 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   const int esize = h->cfg.logits_dtype == BS_BF16 ? 2 : 4;
   const bool aligned = ((uintptr_t)logits % 16 == 0) && ((row_stride_elems * esize) % 16 == 0);
 
+  if (h->cfg.select == BS_SELECT_TWO_PASS) {
+    CFArgs cf;
+    cf.logits = logits;
+    cf.stride = row_stride_elems;
+    cf.V = h->V;
+    cf.W = h->W;
+    cf.K = h->K;
+    cf.KP = h->KP;
+    cf.tile = h->tile;
+    cf.tiles = h->tiles;
+    cf.s = h->st.s;
+    cf.done = h->st.done;
+    cf.pm = h->pm;
+    cf.ps = h->ps;
+    cf.gm = h->gm;
+    cf.qc = h->qc;
+    cf.qj = h->qj;
+    cf.qn = h->qn;
+    cf.cap = h->cap;
+    const dim3 grid(h->tiles, h->rows);
+    if (h->cfg.logits_dtype == BS_BF16) launch_cf_t<uint16_t>(cf, h->ept, aligned, grid, h->stream);
+    else launch_cf_t<float>(cf, h->ept, aligned, grid, h->stream);
+    int rc = launch_status();
+    if (rc != BS_OK) return rc;
+    L3Args a3;
+    a3.cf = cf;
+    fill_k2_args(a3.k2, h, t, beam_idx, token_id, scores, done);
+    if (h->cfg.logits_dtype == BS_BF16) launch_l3_t<uint16_t>(a3, h->kmax, h->stream);
+    else launch_l3_t<float>(a3, h->kmax, h->stream);
+    rc = launch_status();
+    if (rc != BS_OK) return rc;
+    h->t = t;
+    return BS_OK;
+  }
+
   K1Args a1;
   a1.logits = logits;
   a1.stride = row_stride_elems;
@@ -2054,26 +2452,7 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   if (rc != BS_OK) return rc;
 
   K2Args a2;
-  a2.st = h->st;
-  a2.pm = h->pm;
-  a2.ps = h->ps;
-  a2.px = h->px;
-  a2.pv = h->pv;
-  a2.B = h->B;
-  a2.W = h->W;
-  a2.K = h->K;
-  a2.V = h->V;
-  a2.T = h->T;
-  a2.tiles = h->tiles;
-  a2.eos = h->cfg.eos_id;
-  a2.pad = h->cfg.pad_id;
-  a2.stop = h->cfg.stop;
-  a2.alpha = h->cfg.alpha;
-  a2.t = t;
-  a2.out_beam = beam_idx;
-  a2.out_tok = token_id;
-  a2.out_score = scores;
-  a2.out_done = done;
+  fill_k2_args(a2, h, t, beam_idx, token_id, scores, done);
   launch_k2(a2, h->kmax, h->stream);
   rc = launch_status();
   if (rc != BS_OK) return rc;

@@ -62,6 +62,9 @@ def parse():
                     help="verify: minimum accepted block size")
     ap.add_argument("--tile-elems", type=int, default=0, choices=[0, 16, 32, 64],
                     help="logits per thread in the streaming pass (0: the library's choice)")
+    ap.add_argument("--select", default="fused", choices=["fused", "two_pass"],
+                    help="candidate selection: one fused pass (default) or the two-pass "
+                         "coarse-to-fine selection of the LightSeq article")
     ap.add_argument("--kv", default="contig", choices=["contig", "paged"],
                     help="KV cache: contiguous rows (bs_reorder_kv) or block tables with copy "
                          "on write (bs_kv_paged_reorder)")
@@ -123,7 +126,8 @@ def bench_search(args, torch, bs, dev):
         for i in range(s, pool_n, distinct_n):
             pool[i].copy_(src)
     gen_s = time.time() - t0
-    g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems)
+    g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems,
+                                   select=args.select)
     paged = args.kv == "paged"
     bsz = args.block_size
     if paged:
@@ -239,10 +243,11 @@ def bench_search(args, torch, bs, dev):
             "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
                         f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
                         f"gen_len = t" + (", 2W-candidate fill" if args.prune == "top2w" else "")
+                        + (", two-pass selection" if args.select == "two_pass" else "")
                         + (f", paged KV (blocks of {bsz} positions, copy on write)" if paged else ""),
             "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype, "prune": args.prune,
             "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
-            "logit_pool_buffers": pool_n, "kv": args.kv,
+            "logit_pool_buffers": pool_n, "kv": args.kv, "select": args.select,
             **({"block_size": bsz} if paged else {}),
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,

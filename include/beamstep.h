@@ -78,6 +78,21 @@ typedef enum { BS_STOP_TRUE = 0, BS_STOP_HEURISTIC = 1, BS_STOP_NEVER = 2 } bs_s
  *                   the next live slot until W are filled. Needs W <= 8. */
 typedef enum { BS_PRUNE_TOPW = 0, BS_PRUNE_TOP2W = 1 } bs_prune;
 
+/* How the K candidates of each item are found (the result is the same):
+ *   BS_SELECT_FUSED   : one pass over the logits; every tile keeps its own
+ *                       best K and (max, sum exp); the lists are merged.
+ *   BS_SELECT_TWO_PASS: the coarse-to-fine selection of the LightSeq article
+ *                       ("层级式解码计算"): a first pass takes, per row, the
+ *                       maxima of KP >= K groups of logits (KP a power of
+ *                       two) and the log-sum-exp; the K-th largest of the
+ *                       group maxima, R, is at most the row's K-th best
+ *                       logit. A second pass queues every logit >= R with
+ *                       its candidate score s + (x - lse) (the article's
+ *                       queue value leaves out the running score s; it is
+ *                       needed to rank the candidates of an item), and the
+ *                       queue is sorted. It reads the logits twice. */
+typedef enum { BS_SELECT_FUSED = 0, BS_SELECT_TWO_PASS = 1 } bs_select;
+
 typedef struct {
     int32_t batch;        /* B >= 1                                        */
     int32_t beam;         /* W, 1..16                                      */
@@ -93,6 +108,7 @@ typedef struct {
     int32_t tile_elems;   /* logits per thread in the streaming pass:
                              16, 32 or 64; 0 picks one from B, W, V       */
     int32_t prune;        /* bs_prune                                      */
+    int32_t select;       /* bs_select                                     */
 } bs_config;
 
 typedef struct bs_state bs_state;

@@ -85,7 +85,7 @@ def kv_position(wl, b, slot, pos, plane, words):
 
 
 def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_finished=True,
-                 rep=None, tile_elems=0, prune="topw"):
+                 rep=None, tile_elems=0, prune="topw", select="fused"):
     """Run ``steps`` decode steps of workload ``wl`` on the GPU with the oracle
     following along on ``items`` (default: all; items are independent, so a
     sample of them can be followed at full batch size). With ``kv_planes`` > 0
@@ -93,7 +93,8 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     kv_bytes_per_pos], gets position t-1 of every row written and is then
     reordered with gen_len = t each step, and compared bit for bit on the
     followed items. ``prune`` picks the top-W or the 2W-candidate variant on
-    both sides. Returns (Report, gpu search, oracle search)."""
+    both sides; ``select`` the library's selection algorithm (the oracle has
+    one). Returns (Report, gpu search, oracle search)."""
     import torch
     import beam_search_step_amd as bs
 
@@ -101,7 +102,7 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     rep = rep or Report()
     W = wl.beam
-    gpu = bs.BeamSearch.for_workload(wl, tile_elems=tile_elems, prune=prune)
+    gpu = bs.BeamSearch.for_workload(wl, tile_elems=tile_elems, prune=prune, select=select)
     ref = oracle.Search.for_workload(wl.replace(batch=len(items)), prune=prune)
     K = gpu.K
     rows = np.array([b * W + w for b in items for w in range(W)])

@@ -47,7 +47,7 @@ def _cfg(**kw):
 @pytest.mark.parametrize("kw", [
     dict(batch=0), dict(beam=0), dict(beam=17), dict(vocab=0), dict(max_steps=0),
     dict(logits_dtype=2), dict(lp=3), dict(stop=3), dict(num_return=0), dict(num_return=5),
-    dict(tile_elems=8), dict(alpha=float("nan")), dict(beam=16, vocab=2 ** 27),
+    dict(tile_elems=8), dict(alpha=float("nan")), dict(beam=16, vocab=2 ** 27), dict(select=2),
 ])
 def test_create_rejects_invalid_config(kw):
     h = ctypes.c_void_p(123)
@@ -78,11 +78,13 @@ def test_null_arguments_are_rejected():
 
 
 def test_config_struct_layout_matches_header():
-    # offsets of the C struct on x86-64: eight int32, a double, four int32
-    assert ctypes.sizeof(bs.bs_config) == 56
+    # offsets of the C struct on x86-64: eight int32, a double, five int32
+    # (padded to a multiple of 8)
+    assert ctypes.sizeof(bs.bs_config) == 64
     assert bs.bs_config.alpha.offset == 32
     assert bs.bs_config.tile_elems.offset == 48
     assert bs.bs_config.prune.offset == 52
+    assert bs.bs_config.select.offset == 56
     assert ctypes.sizeof(bs.bs_kv_desc) == 48
     # int32 then a pointer (8-aligned), then three int64
     assert ctypes.sizeof(bs.bs_kv_pool) == 40
