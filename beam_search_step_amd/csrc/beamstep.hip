@@ -205,13 +205,21 @@ struct Elem<float> {
     out[2] = v.z;
     out[3] = v.w;
   }
+  __device__ static void unpack(const uint4& v, float* out) {  // 16 bytes: 4 elements
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
 };
 template <>
 struct Elem<uint16_t> {
   static constexpr int kVec = 8;
   __device__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
   __device__ static void loadv(const uint16_t* p, float* out) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    unpack(*reinterpret_cast<const uint4*>(p), out);
+  }
+  __device__ static void unpack(const uint4& v, float* out) {  // 16 bytes: 8 elements
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1656,6 +1664,124 @@ __global__ __launch_bounds__(kThreads) void k4_verify(K4Args a) {
   }
 }
 
+// Verify with one workgroup per row (used when there are enough rows to fill
+// the chip): each thread streams its share of the row, kRowLoads 16-byte
+// loads per batch, all unconditional (indices clamped into the row, so no
+// branch stands between the loads and the compiler waits for a batch only
+// once). A thread visits its columns in increasing order, so a strictly
+// larger logit is the only one that moves its running maximum and the first
+// index of the maximum is kept; a row that is -inf throughout has its first
+// index, 0. For the top-k criterion, logits that beat the proposal's (larger,
+// or equal at a lower index) are counted, in the rare vectors whose maximum
+// reaches it. The row's result goes to the partials as a single tile, for the
+// same accept step.
+constexpr int kRowLoads = 16;
+template <typename T, bool ALIGNED, bool COUNT>
+__global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
+  __shared__ float rx[kWaves];
+  __shared__ int ri[kWaves];
+  __shared__ int rc[kWaves];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
+  const int V = a.V;
+  const int prop = COUNT ? a.proposals[r] : -1;
+  float xp = kInf;  // an out-of-range proposal is beaten by nothing here
+  if (COUNT && prop >= 0 && prop < V) xp = Elem<T>::load1(row + prop);
+  float bx = -kInf;
+  int bi = 0x7fffffff;
+  int cnt = 0;
+  auto count = [&](float x, int v) {
+    if (COUNT) cnt += better(x, v, xp, prop) ? 1 : 0;
+  };
+  if (ALIGNED) {
+    constexpr int VEC = Elem<T>::kVec;
+    const int nvec = V / VEC;
+    const uint4* rv = reinterpret_cast<const uint4*>(row);
+    if (nvec > 0) {  // uniform; a row shorter than one vector has only a tail
+      const int qmax = nvec - 1;
+      for (int q0 = tid; q0 < nvec; q0 += kThreads * kRowLoads) {
+        uint4 raw[kRowLoads];
+#pragma unroll
+        for (int u = 0; u < kRowLoads; ++u) raw[u] = rv[min(q0 + u * kThreads, qmax)];
+#pragma unroll
+        for (int u = 0; u < kRowLoads; ++u) {
+          const int q = q0 + u * kThreads;
+          if (q < nvec) {
+            float x[VEC];
+            Elem<T>::unpack(raw[u], x);
+            float vm = x[0];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+              if (x[k] > bx) {
+                bx = x[k];
+                bi = q * VEC + k;
+              }
+              if (COUNT) vm = fmaxf(vm, x[k]);
+            }
+            if (COUNT && vm >= xp) {
+#pragma unroll
+              for (int k = 0; k < VEC; ++k) count(x[k], q * VEC + k);
+            }
+          }
+        }
+      }
+    }
+    const int v = nvec * VEC + tid;  // the ragged tail, under one vector
+    if (v < V) {  // the tail columns come after every vector column
+      const float x = Elem<T>::load1(row + v);
+      if (x > bx) {
+        bx = x;
+        bi = v;
+      }
+      count(x, v);
+    }
+  } else {
+    for (int v0 = tid; v0 < V; v0 += kThreads * kRowLoads) {
+      float x[kRowLoads];
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) x[u] = Elem<T>::load1(row + min(v0 + u * kThreads, V - 1));
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) {
+        const int v = v0 + u * kThreads;
+        if (v < V) {
+          if (x[u] > bx) {
+            bx = x[u];
+            bi = v;
+          }
+          count(x[u], v);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ox = __shfl_xor(bx, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ox, oi, bx, bi)) {
+      bx = ox;
+      bi = oi;
+    }
+    if (COUNT) cnt += __shfl_xor(cnt, o);
+  }
+  if (lane == 0) {
+    rx[wave] = bx;
+    ri[wave] = bi;
+    rc[wave] = cnt;
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      if (better(rx[w], ri[w], bx, bi)) {
+        bx = rx[w];
+        bi = ri[w];
+      }
+    a.px[r] = bx;
+    a.pv[r] = bi == 0x7fffffff ? 0 : bi;  // every logit -inf: the first index
+    if (COUNT) a.pc[r] = rc[0] + rc[1] + rc[2] + rc[3];
+  }
+}
+
 // the merge as its own launch, one wave per item (a device-scope release and
 // acquire per workgroup, to let the last one merge, cost far more than the
 // second launch on this chip)
@@ -2232,6 +2358,27 @@ void fill_k2_args(K2Args& a2, bs_state* h, int t, int32_t* beam_idx, int32_t* to
   a2.out_done = done;
 }
 
+constexpr int kRowVerifyMinRows = 256;
+
+template <typename T, bool COUNT>
+void launch_k4_row(const K4Args& a, bool aligned, int rows, hipStream_t s) {
+  if (aligned)
+    hipLaunchKernelGGL((k4_row<T, true, COUNT>), dim3(rows), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k4_row<T, false, COUNT>), dim3(rows), dim3(kThreads), 0, s, a);
+}
+
+void launch_k4_tiles(const K4Args& a, int dtype, bool count, bool aligned, dim3 grid,
+                     hipStream_t s) {
+  if (count) {
+    if (dtype == BS_BF16) launch_k4_a<uint16_t, 16, true>(a, aligned, grid, s);
+    else launch_k4_a<float, 16, true>(a, aligned, grid, s);
+  } else {
+    if (dtype == BS_BF16) launch_k4_a<uint16_t, 16, false>(a, aligned, grid, s);
+    else launch_k4_a<float, 16, false>(a, aligned, grid, s);
+  }
+}
+
 int launch_init(bs_state* h) {
   InitArgs ia;
   ia.st = h->st;
@@ -2770,13 +2917,19 @@ int bs_verify_ex(bs_verify_state* h, const void* logits, int64_t row_stride_elem
   a.rank = prop_rank;
   a.top_k = top_k;
   a.min_block = min_block;
-  dim3 grid(h->tiles, h->B * h->k);
-  if (count) {
-    if (h->dtype == BS_BF16) launch_k4_a<uint16_t, 16, true>(a, aligned, grid, h->stream);
-    else launch_k4_a<float, 16, true>(a, aligned, grid, h->stream);
+  const int rows = h->B * h->k;
+  if (rows >= kRowVerifyMinRows) {
+    // enough rows to fill the chip: one workgroup per row, results as one tile
+    a.tiles = 1;
+    if (h->dtype == BS_BF16) {
+      if (count) launch_k4_row<uint16_t, true>(a, aligned, rows, h->stream);
+      else launch_k4_row<uint16_t, false>(a, aligned, rows, h->stream);
+    } else {
+      if (count) launch_k4_row<float, true>(a, aligned, rows, h->stream);
+      else launch_k4_row<float, false>(a, aligned, rows, h->stream);
+    }
   } else {
-    if (h->dtype == BS_BF16) launch_k4_a<uint16_t, 16, false>(a, aligned, grid, h->stream);
-    else launch_k4_a<float, 16, false>(a, aligned, grid, h->stream);
+    launch_k4_tiles(a, h->dtype, count, aligned, dim3(h->tiles, rows), h->stream);
   }
   int rc = launch_status();
   if (rc != BS_OK) return rc;
