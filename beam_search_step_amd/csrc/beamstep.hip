@@ -948,53 +948,44 @@ __global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
   const int c0 = gl * H;    // first tile of this lane
 
   // every load of the item is issued before the first wait: the finished set,
-  // the flags and length penalties, and the partials of the lane's tiles
-  float h_norm = 0.0f, h_raw = 0.0f;
-  int h_len = 0, h_step = 0, h_rank = 0, h_par = 0, h_tok = 0;
-  if (tid < W) {
-    const int e = b * W + tid;
-    h_norm = st.hnorm[e];
-    h_raw = st.hraw[e];
-    h_len = st.hlen[e];
-    h_step = st.hstep[e];
-    h_rank = st.hrank[e];
-    h_par = st.hpar[e];
-    h_tok = st.htok[e];
-  }
+  // the flags and length penalties, and the partials of the lane's tiles.
+  // The loads are unconditional, at indices clamped into range (what a lane
+  // has no use for is masked afterwards): a load under a branch would make
+  // the compiler wait for it before the next one.
+  const int ws = min(tid, W - 1);
+  const int eh = b * W + ws;
+  const float h_norm = st.hnorm[eh], h_raw = st.hraw[eh];
+  const int h_len = st.hlen[eh], h_step = st.hstep[eh], h_rank = st.hrank[eh];
+  const int h_par = st.hpar[eh], h_tok = st.htok[eh];
   const int done = st.done[b];
   const int hcount = st.hcount[b];
   const double lp_t = st.lpt[a.t], lp_T = st.lpt[a.T];
 
-  float sr = -kInf;
+  const int wr = min(w, W - 1);
+  float sr = st.s[b * W + wr];
   float tm[H], ts[H];
   float sc[H][WMAX];
   int col[H][WMAX];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    tm[h] = -kInf;
-    ts[h] = 0.0f;
+    const int64_t pt = (int64_t)(b * W + wr) * tiles + min(c0 + h, tiles - 1);
+    tm[h] = a.pm[pt];
+    ts[h] = a.ps[pt];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
-      sc[h][i] = -kInf;
-      col[h][i] = 0;
+      sc[h][i] = a.px[pt * WMAX + i];
+      col[h][i] = a.pv[pt * WMAX + i];
     }
   }
-  if (w < W) {
-    sr = st.s[b * W + w];
+  if (w >= W) sr = -kInf;  // a group beyond the item's rows
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      if (c0 + h < tiles) {
-        const int64_t pt = (int64_t)(b * W + w) * tiles + c0 + h;
-        tm[h] = a.pm[pt];
-        ts[h] = a.ps[pt];
+  for (int h = 0; h < H; ++h)
+    if (c0 + h >= tiles) {  // a lane beyond the row's tiles
+      tm[h] = -kInf;
+      ts[h] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < WMAX; ++i) {
-          sc[h][i] = a.px[pt * WMAX + i];
-          col[h][i] = a.pv[pt * WMAX + i];
-        }
-      }
+      for (int i = 0; i < WMAX; ++i) sc[h][i] = -kInf;
     }
-  }
   // dead rows (and rows the expand pass skipped) take no part
   const bool live = w < W && sr > -kInf;
   // lse of row w from its tiles' (max, sum exp) partials
@@ -1245,9 +1236,22 @@ __global__ __launch_bounds__(kThreads) void l2_fine(CFArgs a) {
         if (mt > -kInf) S += a.ps[p0 + t] * exp2f((mt - M) * kLog2e);
       }
     S = wave_sum_f(S);
+    // group g's maximum over the row: lane l reads entries l, l+64, ... of
+    // the row's [tiles][KP] maxima, all of group l mod KP (64 is a multiple
+    // of KP), four unconditional loads at a time; then lanes of one group
+    // combine (xor strides >= KP)
+    const int ng = a.tiles * a.KP;
+    const float* gr = a.gm + p0 * a.KP;
     float gv = -kInf;
-    if (lane < a.KP)
-      for (int t = 0; t < a.tiles; ++t) gv = fmaxf(gv, a.gm[(p0 + t) * a.KP + lane]);
+    for (int e0 = lane; e0 < ng; e0 += 4 * 64) {
+      float g4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) g4[u] = gr[min(e0 + u * 64, ng - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u * 64 < ng) gv = fmaxf(gv, g4[u]);
+    }
+    for (int st = a.KP; st < 64; st <<= 1) gv = fmaxf(gv, __shfl_xor(gv, st));
     int gt = 0, ge = 0;
     for (int q = 0; q < a.KP; ++q) {
       const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), q));
@@ -1362,13 +1366,19 @@ __global__ __launch_bounds__(kThreads) void l3_sort_finalize(L3Args args) {
     return;
   }
   if (n <= cf.cap) {
-    uint64_t k[kPer];
+    // unconditional loads (the queue has cap entries; those at or past n are
+    // masked), so that they are all in flight before the first wait
+    float qc[kPer];
+    int qj[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int e = q * kThreads + tid;
-      k[q] = 0;
-      if (e < n) k[q] = pack_key(cf.qc[(int64_t)b * cf.cap + e], cf.qj[(int64_t)b * cf.cap + e]);
+      const int e = min(q * kThreads + tid, cf.cap - 1);
+      qc[q] = cf.qc[(int64_t)b * cf.cap + e];
+      qj[q] = cf.qj[(int64_t)b * cf.cap + e];
     }
+    uint64_t k[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) k[q] = (q * kThreads + tid < n) ? pack_key(qc[q], qj[q]) : 0;
     block_topk<kPer>(k, K, wbest, best);
   } else {
     // exact fallback: the lse of each live row, then K rounds over all of the
@@ -1921,6 +1931,7 @@ __global__ __launch_bounds__(kThreads) void k6_paged_reorder(K6Args a) {
   __shared__ int told[kPagedMaxTable];
   __shared__ int tnew[kPagedMaxTable];
   __shared__ int par[kMaxBeam];
+  __shared__ int plan_sh[2 + 2 * kMaxBeam];
   __shared__ int nfree_sh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int W = a.W, mb = a.mb, bpi = a.bpi, t = a.t, bs = a.bs;
@@ -1937,15 +1948,16 @@ __global__ __launch_bounds__(kThreads) void k6_paged_reorder(K6Args a) {
     const int v = pg.table[(int64_t)b * nt + e];
     told[e] = (v >= base && v < base + bpi) ? v : -1;  // only the item's own blocks
   }
+  if (tid < 2 + 2 * kMaxBeam) plan_sh[tid] = plan[tid];  // staged with the other loads
+  if (tid == 0) nfree_sh = nf;
+  __syncthreads();
   if (tid < W) {  // parent of each slot: itself unless the plan moves it
     int pp = tid;
-    const int nsrc = plan[0];
-    if (plan[1] > 0)
-      for (int q = 0; q < nsrc; ++q)
-        if ((plan[2 + kMaxBeam + q] >> tid) & 1) pp = plan[2 + q];
+    if (plan_sh[1] > 0)
+      for (int q = 0; q < plan_sh[0]; ++q)
+        if ((plan_sh[2 + kMaxBeam + q] >> tid) & 1) pp = plan_sh[2 + q];
     par[tid] = pp;
   }
-  if (tid == 0) nfree_sh = nf;
   __syncthreads();
 
   // new table: a live slot of a running item takes its parent's blocks
