@@ -396,13 +396,13 @@ def copy_reference(torch, dev):
 
 
 def k3_source_hash():
-    """Hash of the KV-reorder kernel's source: counter readings are only used
-    while the kernel they were taken on is unchanged."""
+    """Hash of the KV-reorder kernel's source (csrc/kv_reorder.h from its
+    section header on): counter readings are only used while the kernel they
+    were taken on is unchanged."""
     import hashlib
-    src = open(os.path.join(ROOT, "beam_search_step_amd", "csrc", "beamstep.hip")).read()
+    src = open(os.path.join(ROOT, "beam_search_step_amd", "csrc", "kv_reorder.h")).read()
     i = src.index("// K3: in-place KV reorder")
-    j = src.index("// K4: blockwise verify")
-    return hashlib.sha256(src[i:j].encode()).hexdigest()[:16]
+    return hashlib.sha256(src[i:].encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):

@@ -149,6 +149,19 @@ def test_wide_beam_sampled_items(dev, tile_elems):
     g.close()
 
 
+@pytest.mark.parametrize("select", ["fused", "two_pass"])
+def test_vocab_above_a_million(dev, select):
+    """V = 1.2M with 16 logits per thread: 293 tiles per row, more than the
+    tile-list merge takes, so the general merge kernel runs (fused); the
+    two-pass selection has no tile limit."""
+    wl = synth.WORKLOADS["tbase"].replace(batch=2, beam=3, vocab=1_200_000, eos_id=7,
+                                          eos_in_zipf=False, eos_ramp=9.0, ramp_steps=2,
+                                          max_steps=4, name="bigv")
+    rep, g, ref = run_stepwise(wl, 4, dev, kv_planes=1, tile_elems=16, select=select)
+    compare_final(g, ref, range(wl.batch), 1, f"V=1.2M {select}")
+    g.close()
+
+
 # ---------------------------------------------------------------------------
 # Hugging Face 2W-candidate variant
 # ---------------------------------------------------------------------------
