@@ -1,37 +1,42 @@
-// beamstep.hip -- HIP kernels and host runtime of libbeamstep.so (gfx950).
+// beamstep.hip -- host runtime of libbeamstep.so (gfx950), and the one
+// translation unit that includes the kernels.
 //
 // One decode step of batched beam search ("llm_internals" 9.2.2: expand,
 // score, prune, finalize; the batched section of "Transformers中的Beam
-// Search高效实现") as three kernels per step, plus the verify step of
-// blockwise parallel decoding ("Blockwise Parallel Decoding", section 3):
+// Search高效实现") as two kernels plus the KV-cache reorder, and the verify
+// step of blockwise parallel decoding ("Blockwise Parallel Decoding",
+// section 3):
 //
-//   K1 expand_select   grid (tiles, rows). Streams each live row's logits once
-//                      with 16-byte loads. Per (row, tile) it leaves the
-//                      online softmax partial (max m, sum exp(x - m)) and the
-//                      tile's W best raw logits ordered by (x desc, v asc).
-//                      Log-softmax is monotone within a row, so the union of
-//                      the tile lists holds the row's top-W candidates (the
-//                      same argument as the coarse-to-fine selection in the
-//                      LightSeq article, "层级式解码计算").
-//   K2 merge_finalize  grid (B). Combines the partials into lse per row,
-//                      forms cand = fp32(s + fp32(x - lse)) for the W*tiles*W
-//                      listed candidates, takes the top-W by (cand desc, j
-//                      asc), then runs the finalize sub-step: EOS selections
-//                      into the finished set with the length penalty,
-//                      compaction of live slots in rank order, backpointers,
-//                      the stop rule, and the plan for the KV reorder.
-//   K3 kv_reorder      grid (tiles, B, planes). Each thread reads one 16-byte
-//                      word of every distinct parent row, waits, and writes it
-//                      to every slot that moved, so swaps and cycles are safe
-//                      in place and a shared parent is read once.
-//   K4 verify          grid (tiles, rows) argmax partials (and, for the top-k
-//                      criterion, counts of logits beating the proposal), then
-//                      one wave per item merges them and forms the accepted
-//                      prefix.
-//   K5 finalize        grid (B). Final ranking and backtrace of the tokens.
+//   K1 expand_select   (select_fused.h) grid (tiles, rows). Streams each live
+//                      row's logits once with 16-byte loads. Per (row, tile)
+//                      it leaves the online softmax partial (max m, sum
+//                      exp(x - m)) and the tile's K best raw logits ordered by
+//                      (x desc, v asc). Log-softmax is monotone within a row,
+//                      so the union of the tile lists holds the row's best K
+//                      candidates.
+//   K2 select_finalize (select_fused.h) grid (B). lse per row from the
+//                      partials, a K-round merge of the sorted tile lists per
+//                      row and then across rows by (cand desc, j asc), then the
+//                      finalize sub-step: EOS selections into the finished set
+//                      with the length penalty, compaction of live slots in
+//                      rank order, backpointers, the stop rule, and the plan
+//                      for the KV reorder.
+//   K3 kv_reorder      (kv_reorder.h) grid (tiles, B, planes). Each thread
+//                      reads one 16-byte word of every distinct parent row,
+//                      waits, and writes it to every slot that moved, so swaps
+//                      and cycles are safe in place and a shared parent is
+//                      read once.
+//   K4 verify          (verify.h) argmax and proposal ranks per row, then one
+//                      wave per item forms the accepted prefix.
+//   K5 finalize        (search_state.h) grid (B). Final ranking and backtrace.
+//   L1-L3              (select_two_pass.h) the coarse-to-fine selection of the
+//                      LightSeq article ("层级式解码计算"), selectable instead
+//                      of K1/K2.
+//   K6/K7              (kv_paged.h) the paged KV cache: block tables and the
+//                      copies on write.
 //
 // No matrix cores: nothing here is a dense contraction. Every kernel is bound
-// by HBM bandwidth.
+// by HBM bandwidth or, at small shapes, by latency.
 
 #include <hip/hip_runtime.h>
 
