@@ -286,13 +286,21 @@ void fill_k2_args(K2Args& a2, bs_state* h, int t, int32_t* beam_idx, int32_t* to
 }
 
 constexpr int kRowVerifyMinRows = 256;
+constexpr int kVerifySegWorkgroups = 1024;
+// row segments of the verify row kernel: enough workgroups to keep every CU
+// streaming, never more than the tiles the partials hold
+int verify_segments(int rows, int tiles) {
+  const int want = (kVerifySegWorkgroups + rows - 1) / rows;
+  return want < 1 ? 1 : (want > tiles ? tiles : want);
+}
 
 template <typename T, bool COUNT>
 void launch_k4_row(const K4Args& a, bool aligned, int rows, hipStream_t s) {
+  const dim3 grid(a.tiles, rows);  // segments x rows
   if (aligned)
-    hipLaunchKernelGGL((k4_row<T, true, COUNT>), dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k4_row<T, true, COUNT>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k4_row<T, false, COUNT>), dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k4_row<T, false, COUNT>), grid, dim3(kThreads), 0, s, a);
 }
 
 void launch_k4_tiles(const K4Args& a, int dtype, bool count, bool aligned, dim3 grid,
@@ -846,8 +854,8 @@ int bs_verify_ex(bs_verify_state* h, const void* logits, int64_t row_stride_elem
   a.min_block = min_block;
   const int rows = h->B * h->k;
   if (rows >= kRowVerifyMinRows) {
-    // enough rows to fill the chip: one workgroup per row, results as one tile
-    a.tiles = 1;
+    // enough rows to fill the chip: a few segments per row, one tile each
+    a.tiles = verify_segments(rows, h->tiles);
     if (h->dtype == BS_BF16) {
       if (count) launch_k4_row<uint16_t, true>(a, aligned, rows, h->stream);
       else launch_k4_row<uint16_t, false>(a, aligned, rows, h->stream);

@@ -134,26 +134,29 @@ __global__ __launch_bounds__(kThreads) void k4_verify(K4Args a) {
   }
 }
 
-// Verify with one workgroup per row (used when there are enough rows to fill
-// the chip): each thread streams its share of the row, kRowLoads 16-byte
-// loads per batch, all unconditional (indices clamped into the row, so no
-// branch stands between the loads and the compiler waits for a batch only
-// once). A thread visits its columns in increasing order, so a strictly
-// larger logit is the only one that moves its running maximum and the first
-// index of the maximum is kept; a row that is -inf throughout has its first
-// index, 0. For the top-k criterion, logits that beat the proposal's (larger,
-// or equal at a lower index) are counted, in the rare vectors whose maximum
-// reaches it. The row's result goes to the partials as a single tile, for the
-// same accept step.
+// Verify by row segments (used when there are enough rows to fill the chip):
+// grid (segments, rows), a workgroup streams one contiguous segment of a row,
+// kRowLoads 16-byte loads per thread per batch, all unconditional (indices
+// clamped into the segment, so no branch stands between the loads and the
+// compiler waits for a batch only once). A thread visits its columns in
+// increasing order, so a strictly larger logit is the only one that moves its
+// running maximum and the first index of the maximum is kept; a segment that
+// is -inf throughout reports its first column, so that a row that is -inf
+// throughout has its first index, 0, after the merge. For the top-k criterion,
+// logits that beat the proposal's (larger, or equal at a lower index) are
+// counted, in the rare vectors whose maximum reaches it. Segment s of row r
+// is tile s of the partials, for the same accept step.
 constexpr int kRowLoads = 16;
 template <typename T, bool ALIGNED, bool COUNT>
 __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
   __shared__ float rx[kWaves];
   __shared__ int ri[kWaves];
   __shared__ int rc[kWaves];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, seg = blockIdx.x, nseg = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const int V = a.V;
+  int first;  // the segment's first column
   const int prop = COUNT ? a.proposals[r] : -1;
   float xp = kInf;  // an out-of-range proposal is beaten by nothing here
   if (COUNT && prop >= 0 && prop < V) xp = Elem<T>::load1(row + prop);
@@ -166,17 +169,20 @@ __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
   if (ALIGNED) {
     constexpr int VEC = Elem<T>::kVec;
     const int nvec = V / VEC;
+    // vectors [qs, qe) of the row; the ragged tail goes with the last segment
+    const int qs = (int)((int64_t)nvec * seg / nseg), qe = (int)((int64_t)nvec * (seg + 1) / nseg);
+    first = qs * VEC;
     const uint4* rv = reinterpret_cast<const uint4*>(row);
-    if (nvec > 0) {  // uniform; a row shorter than one vector has only a tail
-      const int qmax = nvec - 1;
-      for (int q0 = tid; q0 < nvec; q0 += kThreads * kRowLoads) {
+    if (qe > qs) {  // uniform; an empty segment (a row of few vectors) has none
+      const int qmax = qe - 1;
+      for (int q0 = qs + tid; q0 < qe; q0 += kThreads * kRowLoads) {
         uint4 raw[kRowLoads];
 #pragma unroll
         for (int u = 0; u < kRowLoads; ++u) raw[u] = rv[min(q0 + u * kThreads, qmax)];
 #pragma unroll
         for (int u = 0; u < kRowLoads; ++u) {
           const int q = q0 + u * kThreads;
-          if (q < nvec) {
+          if (q < qe) {
             float x[VEC];
             Elem<T>::unpack(raw[u], x);
             float vm = x[0];
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
       }
     }
     const int v = nvec * VEC + tid;  // the ragged tail, under one vector
-    if (v < V) {  // the tail columns come after every vector column
+    if (seg == nseg - 1 && v < V) {  // the tail columns come after every vector column
       const float x = Elem<T>::load1(row + v);
       if (x > bx) {
         bx = x;
@@ -206,14 +212,17 @@ __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
       count(x, v);
     }
   } else {
-    for (int v0 = tid; v0 < V; v0 += kThreads * kRowLoads) {
+    // columns [vs, ve) of the row
+    const int vs = (int)((int64_t)V * seg / nseg), ve = (int)((int64_t)V * (seg + 1) / nseg);
+    first = vs;
+    for (int v0 = vs + tid; v0 < ve; v0 += kThreads * kRowLoads) {
       float x[kRowLoads];
 #pragma unroll
-      for (int u = 0; u < kRowLoads; ++u) x[u] = Elem<T>::load1(row + min(v0 + u * kThreads, V - 1));
+      for (int u = 0; u < kRowLoads; ++u) x[u] = Elem<T>::load1(row + min(v0 + u * kThreads, ve - 1));
 #pragma unroll
       for (int u = 0; u < kRowLoads; ++u) {
         const int v = v0 + u * kThreads;
-        if (v < V) {
+        if (v < ve) {
           if (x[u] > bx) {
             bx = x[u];
             bi = v;
@@ -246,9 +255,10 @@ __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
         bx = rx[w];
         bi = ri[w];
       }
-    a.px[r] = bx;
-    a.pv[r] = bi == 0x7fffffff ? 0 : bi;  // every logit -inf: the first index
-    if (COUNT) a.pc[r] = rc[0] + rc[1] + rc[2] + rc[3];
+    const int64_t pt = (int64_t)r * nseg + seg;
+    a.px[pt] = bx;
+    a.pv[pt] = bi == 0x7fffffff ? first : bi;  // every logit -inf: the first column
+    if (COUNT) a.pc[pt] = rc[0] + rc[1] + rc[2] + rc[3];
   }
 }
 

@@ -273,12 +273,15 @@ def test_verify_topk_edge_cases(dev):
     bf16 and unaligned strides for the counting path."""
     import beam_search_step_amd as bs
     rng = np.random.default_rng(17)
-    # the first four run the per-tile kernel, the last four (>= 256 rows) the
-    # one-workgroup-per-row kernel
+    # the first four run the per-tile kernel, the rest (>= 256 rows) the row
+    # kernel, over one or more segments per row (16-byte aligned rows with a
+    # ragged tail among them)
     for (B, k, V, dtype, pad) in [(3, 5, 9, "f32", 0), (2, 3, 4097, "f32", 2),
                                   (4, 16, 300, "bf16", 0), (1, 8, 70001, "bf16", 5),
                                   (256, 1, 9, "f32", 0), (32, 8, 4097, "f32", 2),
-                                  (16, 16, 300, "bf16", 0), (64, 4, 70001, "bf16", 5)]:
+                                  (16, 16, 300, "bf16", 0), (64, 4, 70001, "bf16", 5),
+                                  (128, 4, 12301, "bf16", 3), (512, 1, 20000, "f32", 0),
+                                  (32, 8, 8195, "f32", 1)]:
         x = rng.integers(-3, 3, size=(B, k, V)).astype(np.float32)   # many ties
         x[0, 0] = -np.inf
         if dtype == "bf16":
@@ -314,7 +317,8 @@ def test_verify_edge_cases(dev):
     for (B, k, V, dtype) in [(3, 5, 9, "f32"), (2, 1, 4097, "f32"), (4, 64, 300, "bf16"),
                              (1, 8, 70001, "bf16"), (300, 1, 4097, "f32"),
                              (8, 64, 300, "bf16"), (64, 4, 70001, "bf16"),
-                             (256, 1, 4099, "bf16")]:
+                             (256, 1, 4099, "bf16"), (128, 4, 16000, "f32"),
+                             (64, 8, 24576, "bf16"), (256, 2, 8200, "f32")]:
         x = rng.integers(-3, 3, size=(B, k, V)).astype(np.float32)   # many ties
         x[0, 0] = -np.inf                                           # an all -inf row
         if dtype == "bf16":
