@@ -157,7 +157,7 @@ def bench_search(args, torch, bs, dev):
         if paged:
             pk.reset()
 
-    def run(n, record):
+    def run(n, record, with_events=False):
         ts = []
         for i in range(n):
             t = (g.steps % T) + 1
@@ -165,66 +165,80 @@ def bench_search(args, torch, bs, dev):
                 reset()
             o = hist[i] if record else hist[0]
             bs.bs_step(g.h, pool[(t - 1) % pool_n], *o)
-            if record and args.events:
+            if with_events:
                 events[i][0].record(stream)
             if paged:
                 bs.bs_kv_paged_reorder(pk.h, desc, t)
             else:
                 bs.bs_reorder_kv(g.h, desc, t)
-            if record and args.events:
+            if with_events:
                 events[i][1].record(stream)
             ts.append(t)
         return ts
 
-    # warmup (untimed), then the timed region
-    reset()
-    run(args.warmup, False)
-    reset()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    ts = run(args.steps, True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    def timed(with_events):
+        """The same K steps from a fresh search: wall time, the step numbers
+        run and the algorithmic bytes of every step."""
+        reset()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        ts = run(args.steps, True, with_events)
+        torch.cuda.synchronize()
+        return ts, time.perf_counter() - t_start, alg_bytes(ts)
 
     # ---- algorithmic bytes from the recorded step outputs -----------------------
-    bi = hist_bi.cpu().numpy()
-    sc = hist_sc.cpu().numpy()
-    dn = hist_dn.cpu().numpy().astype(bool)
-    kv_bytes = []
-    logit_bytes = []
-    prev_live = np.zeros((B, W), bool)
-    for i, t in enumerate(ts):
-        if t == 1:
-            prev_live = np.zeros((B, W), bool)
-            prev_live[:, 0] = True
-        live_rows = int(prev_live.sum())                  # rows the step had to read
-        logit_bytes.append(live_rows * V * wl.elem_bytes + 20 * B * W)
-        if paged:
-            # copies on write: live slots beyond the first of each parent,
-            # t % block_size positions each, read and written in every pool;
-            # plus the items' tables, reference counts and free lists
-            copies = 0
-            if t % bsz:
+    def alg_bytes(ts):
+        bi = hist_bi.cpu().numpy()
+        sc = hist_sc.cpu().numpy()
+        dn = hist_dn.cpu().numpy().astype(bool)
+        kv_b, logit_b = step_bytes(ts, bi, sc, dn)
+        return kv_b, logit_b, int((~dn).sum())
+
+    def step_bytes(ts, bi, sc, dn):
+        kv_bytes = []
+        logit_bytes = []
+        prev_live = np.zeros((B, W), bool)
+        for i, t in enumerate(ts):
+            if t == 1:
+                prev_live = np.zeros((B, W), bool)
+                prev_live[:, 0] = True
+            live_rows = int(prev_live.sum())                  # rows the step had to read
+            logit_bytes.append(live_rows * V * wl.elem_bytes + 20 * B * W)
+            if paged:
+                # copies on write: live slots beyond the first of each parent,
+                # t % block_size positions each, read and written in every pool;
+                # plus the items' tables, reference counts and free lists
+                copies = 0
+                if t % bsz:
+                    for b in range(B):
+                        if dn[i, b]:
+                            continue
+                        lv = [w for w in range(W) if sc[i, b, w] > -np.inf]
+                        copies += len(lv) - len({int(bi[i, b, w]) for w in lv})
+                kv_bytes.append(2 * copies * (t % bsz) * bpp * planes_n
+                                + 2 * B * (W * pk.max_blocks + 2 * pk.blocks_per_item) * 4)
+            else:
+                moved_total = 0
                 for b in range(B):
                     if dn[i, b]:
                         continue
-                    lv = [w for w in range(W) if sc[i, b, w] > -np.inf]
-                    copies += len(lv) - len({int(bi[i, b, w]) for w in lv})
-            kv_bytes.append(2 * copies * (t % bsz) * bpp * planes_n
-                            + 2 * B * (W * pk.max_blocks + 2 * pk.blocks_per_item) * 4)
-        else:
-            moved_total = 0
-            for b in range(B):
-                if dn[i, b]:
-                    continue
-                live = sc[i, b] > -np.inf
-                moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
-                parents = {int(bi[i, b, w]) for w in moved}
-                moved_total += len(moved) + len(parents)
-            kv_bytes.append(moved_total * t * bpp * planes_n)
-        prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
-    kv_bytes = np.array(kv_bytes, np.float64)
-    logit_bytes = np.array(logit_bytes, np.float64)
+                    live = sc[i, b] > -np.inf
+                    moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
+                    parents = {int(bi[i, b, w]) for w in moved}
+                    moved_total += len(moved) + len(parents)
+                kv_bytes.append(moved_total * t * bpp * planes_n)
+            prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
+        return np.array(kv_bytes, np.float64), np.array(logit_bytes, np.float64)
+
+    # warmup (untimed); the timed region, which records no events, since each
+    # event record stalls the GPU for several microseconds between kernels;
+    # then, for the per-launch durations, the same K steps with a pair of
+    # events around every reorder launch
+    reset()
+    run(args.warmup, False)
+    ts, elapsed, (kv_bytes, logit_bytes, live_item_steps) = timed(False)
+    if args.events:
+        _, elapsed_ev, (kv_bytes_ev, logit_bytes_ev, _) = timed(True)
 
     out = {
         "metric": METRIC,
@@ -251,7 +265,7 @@ def bench_search(args, torch, bs, dev):
             **({"block_size": bsz} if paged else {}),
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
-        "live_item_steps": int((~dn).sum()),
+        "live_item_steps": live_item_steps,
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if args.events:
@@ -259,32 +273,34 @@ def bench_search(args, torch, bs, dev):
         # between one step's reorder and the next: bs_step's two kernels
         d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
                            for i in range(1, len(events))]) * 1e-3
-        ach = kv_bytes.sum() / d_kv.sum() / 1e9
-        step_gbs = logit_bytes[1:].sum() / d_step.sum() / 1e9
+        ach = kv_bytes_ev.sum() / d_kv.sum() / 1e9
+        step_gbs = logit_bytes_ev[1:].sum() / d_step.sum() / 1e9
         if paged:
             # the logits pass dominates once the reorder moves only partial blocks
             out["roofline"] = {
                 "bound": "hbm", "kernel": "k1_expand_select + k2_select_finalize",
                 "achieved": step_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": step_gbs / PEAK_HBM_GBS, "traffic": None,
-                "alg_bytes_per_launch": logit_bytes.mean(), "avg_launch_us": 1e6 * d_step.mean(),
+                "alg_bytes_per_launch": logit_bytes_ev.mean(), "avg_launch_us": 1e6 * d_step.mean(),
             }
             out["paged_reorder"] = {
                 "kernels": "k6_paged_reorder + k7_paged_copy", "avg_us": 1e6 * d_kv.mean(),
-                "alg_bytes_per_step": kv_bytes.mean(), "alg_gbs": ach,
+                "alg_bytes_per_step": kv_bytes_ev.mean(), "alg_gbs": ach,
             }
         else:
             out["roofline"] = {
                 "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                 "traffic": measured_traffic(wl.name),
-                "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
+                "alg_bytes_per_launch": kv_bytes_ev.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
             }
         out["step_kernels"] = {
             "kernels": "k1_expand_select + k2 (event gap between reorders)",
             "avg_us": 1e6 * d_step.mean(),
             "alg_gbs": step_gbs,
         }
+        # the events pass: the same steps, slower by the event records' stalls
+        out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
@@ -319,16 +335,22 @@ def bench_verify(args, torch, bs, dev):
     vk = dict(top_k=args.verify_top_k, min_block=args.verify_min_block)
     for i in range(args.warmup):
         ver(lgs[i % pool_n], props[i % pool_n], **vk)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        if args.events:
-            events[i][0].record(stream)
-        ver(lgs[i % pool_n], props[i % pool_n], **vk)
-        if args.events:
-            events[i][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    def timed(with_events):
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            if with_events:
+                events[i][0].record(stream)
+            ver(lgs[i % pool_n], props[i % pool_n], **vk)
+            if with_events:
+                events[i][1].record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_start
+
+    # the timed region records no events (each record stalls the GPU for
+    # several microseconds); a second pass brackets every call with events
+    elapsed = timed(False)
+    elapsed_ev = timed(True) if args.events else None
     alg = Bv * k * V * 4 + Bv * k * 4 * 2 + Bv * 4
     out = {
         "metric": "blockwise verify calls/sec and achieved HBM GB/s (% of peak); 1 GPU",
@@ -348,6 +370,7 @@ def bench_verify(args, torch, bs, dev):
                            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": ach / PEAK_HBM_GBS, "traffic": None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
+        out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     # model calls per generated token implied by the mean accepted block k^
     # ("Blockwise Parallel Decoding" section 4): separate predict and verify
     # calls cost 2/k^ per token; merging verify n with predict n+1 costs 1/k^
