@@ -366,7 +366,7 @@ def bench_verify(args, torch, bs, dev):
     if args.events:
         d = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
         ach = alg / d.mean() / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": "k4_argmax_tiles + k4_accept",
+        out["roofline"] = {"bound": "hbm", "kernel": "k4_row (row segments) + k4_accept, one call",
                            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": ach / PEAK_HBM_GBS, "traffic": None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
