@@ -72,7 +72,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
     ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-steps", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle baseline: time budget of its sample (steps run until it is spent)")
     ap.add_argument("--events", type=int, default=1,
                     help="record HIP events around each KV-reorder launch (roofline)")
     ap.add_argument("--copy-reference", type=int, default=1,
@@ -302,7 +303,7 @@ def bench_search(args, torch, bs, dev):
         # the events pass: the same steps, slower by the event records' stalls
         out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, bpp, planes_n, args.prune)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
     if paged:
         ov, _ = pk.status()
@@ -384,11 +385,12 @@ def bench_verify(args, torch, bs, dev):
     }
     if not args.no_cpu_baseline:
         import oracle
+        pin_one_core()
         lg0 = lgs[0].cpu().numpy()
         pr0 = props[0].cpu().numpy()
         t0 = time.perf_counter()
         n = 0
-        while time.perf_counter() - t0 < 2.0:
+        while time.perf_counter() - t0 < args.cpu_seconds:
             oracle.verify_ex(lg0, pr0, **vk)
             n += 1
         dt = time.perf_counter() - t0
@@ -443,27 +445,36 @@ def measured_traffic(workload):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, n_steps, bpp, planes_n, prune="topw"):
-    """The CPU oracle, single-threaded on one core, on a bounded sample: the
-    first n_steps decode steps of the same search (select + apply over all
-    items), each followed by the oracle's KV gather over every plane at
-    gen_len = max_steps / 2 (the mean gen_len of a full search)."""
-    import oracle
-    import synth
-
+def pin_one_core():
     try:
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     except (AttributeError, OSError):
         pass
+
+
+def cpu_baseline(wl, seconds, bpp, planes_n, prune="topw"):
+    """The CPU oracle, single-threaded on one core, on a bounded sample: decode
+    steps 1, 2, ... of the same search (select + apply over all items), each
+    followed by the oracle's KV gather over every plane at gen_len =
+    max_steps / 2 (the mean gen_len of a full search), until ``seconds`` of
+    oracle time are spent. Each step's logits are generated outside the timing."""
+    import oracle
+    import synth
+
+    pin_one_core()
     ref = oracle.Search.for_workload(wl, prune=prune)
     gen = wl.max_steps // 2
     host = [np.zeros((wl.rows, gen, bpp), np.uint8) for _ in range(planes_n)]
-    lgs = [synth.logits(wl, t) for t in range(1, n_steps + 1)]
-    t0 = time.perf_counter()
-    for lg in lgs:
+    dt, n_steps = 0.0, 0
+    for t in range(1, wl.max_steps + 1):
+        lg = synth.logits(wl, t)
+        t0 = time.perf_counter()
         bi, tk, sc, dn = ref.step(lg)
         oracle.kv_reorder(host, bi, dn, gen)
-    dt = time.perf_counter() - t0
+        dt += time.perf_counter() - t0
+        n_steps = t
+        if dt >= seconds or dn.all():
+            break
     return {"value": n_steps / dt, "unit": "beam steps/s", "cores": 1, "kind": "oracle",
             "sample": f"oracle steps 1-{n_steps} of the B={wl.batch} W={wl.beam} V={wl.vocab} "
                       f"search (select + apply on all items), each with the KV gather of "
