@@ -27,6 +27,7 @@ times the CPU oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -153,27 +154,45 @@ def bench_search(args, torch, bs, dev):
               for _ in range(args.steps if args.events else 0)]
     hist = [(hist_bi[i], hist_tk[i], hist_sc[i], hist_dn[i]) for i in range(n_hist)]
 
+    # the timed loop calls the C entry points directly, with every pointer
+    # computed beforehand, so that the host issues a step in a few
+    # microseconds: the early steps of a search take the GPU less time than
+    # the Python wrappers would take to issue them
+    L = bs.library()
+    h = g.h
+    ph = pk.h if paged else None
+    pool_ptrs = [pool[i].data_ptr() for i in range(pool_n)]
+    row_stride = pool.stride(1)
+    hist_ptrs = [tuple(x.data_ptr() for x in o) for o in hist]
+    desc_ref = ctypes.byref(desc)
+    step_c, kv_c = L.bs_step, (L.bs_kv_paged_reorder if paged else L.bs_reorder_kv)
+    kv_h = ph if paged else h
+    taken = [0]  # steps of the current search (the library's own count)
+
     def reset():
         g.reset()
         if paged:
             pk.reset()
+        taken[0] = 0
 
     def run(n, record, with_events=False):
         ts = []
         for i in range(n):
-            t = (g.steps % T) + 1
-            if t == 1 and g.steps:
+            t = taken[0] % T + 1
+            if t == 1 and taken[0]:
                 reset()
-            o = hist[i] if record else hist[0]
-            bs.bs_step(g.h, pool[(t - 1) % pool_n], *o)
+            o = hist_ptrs[i] if record else hist_ptrs[0]
+            rc = step_c(h, pool_ptrs[(t - 1) % pool_n], row_stride, *o)
+            if rc:
+                raise bs.BeamStepError(rc, "bs_step")
             if with_events:
                 events[i][0].record(stream)
-            if paged:
-                bs.bs_kv_paged_reorder(pk.h, desc, t)
-            else:
-                bs.bs_reorder_kv(g.h, desc, t)
+            rc = kv_c(kv_h, desc_ref, t)
+            if rc:
+                raise bs.BeamStepError(rc, "reorder")
             if with_events:
                 events[i][1].record(stream)
+            taken[0] = t
             ts.append(t)
         return ts
 
@@ -336,13 +355,30 @@ def bench_verify(args, torch, bs, dev):
     vk = dict(top_k=args.verify_top_k, min_block=args.verify_min_block)
     for i in range(args.warmup):
         ver(lgs[i % pool_n], props[i % pool_n], **vk)
+    # the timed loop calls the C entry point directly with precomputed pointers
+    L = bs.library()
+    lg_ptrs = [x.data_ptr() for x in lgs]
+    pr_ptrs = [x.data_ptr() for x in props]
+    acc_ptr, am_ptr = ver.accept_len.data_ptr(), ver.argmax.data_ptr()
+    exact = vk["top_k"] == 1 and vk["min_block"] == 0
+
+    def call(i):
+        j = i % pool_n
+        if exact:
+            rc = L.bs_verify(ver.h, lg_ptrs[j], V, pr_ptrs[j], acc_ptr, am_ptr)
+        else:
+            rc = L.bs_verify_ex(ver.h, lg_ptrs[j], V, pr_ptrs[j], vk["top_k"], vk["min_block"],
+                                acc_ptr, am_ptr, None)
+        if rc:
+            raise bs.BeamStepError(rc, "bs_verify")
+
     def timed(with_events):
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for i in range(args.steps):
             if with_events:
                 events[i][0].record(stream)
-            ver(lgs[i % pool_n], props[i % pool_n], **vk)
+            call(i)
             if with_events:
                 events[i][1].record(stream)
         torch.cuda.synchronize()
