@@ -48,7 +48,7 @@ METRIC = "beam steps/sec and achieved HBM GB/s (% of peak) at B,W,V; 1 GPU"
 POOLS = {"llama3_8b": (64, 16), "tbase": (128, 128), "wide": (3, 3)}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
@@ -79,11 +79,11 @@ def parse():
                     help="record HIP events around each KV-reorder launch (roofline)")
     ap.add_argument("--copy-reference", type=int, default=1,
                     help="time a plain 1 GiB device copy after the timed region")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the beam-step "
