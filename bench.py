@@ -440,7 +440,7 @@ def bench_verify(args, torch, bs, dev):
 
 def copy_reference(torch, dev):
     """A plain device copy of 1 GiB (torch's copy kernel): the practical
-    read+write HBM rate on this machine, for comparison with the KV reorder."""
+    read+write HBM rate of this GPU, for comparison with the KV reorder."""
     n = 1 << 30
     a = torch.empty(n // 2, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
