@@ -373,9 +373,8 @@ class BeamSearch:
 class PagedKV:
     """Block tables with copy on write for a BeamSearch's KV cache.
 
-    ``table()`` is the device table as a torch tensor [B*W, max_blocks]
-    (a view of the library's buffer); ``reorder(pools, t)`` follows the
-    bs_step of step t.
+    ``table()`` returns a copy of the device table as a torch tensor
+    [B*W, max_blocks]; ``reorder(pools, t)`` follows the bs_step of step t.
     """
 
     def __init__(self, search: "BeamSearch", block_size: int, blocks_per_item: int = 0):
