@@ -212,8 +212,9 @@ void launch_k2(const K2Args& a, int wmax, hipStream_t s) {
 // ---- K3 dispatch ----------------------------------------------------------
 template <int WMAX, int WORD, bool CONTIG>
 void launch_k3_c(const K3Args& a, int64_t tiles_per_row, int B, int nplanes, hipStream_t s) {
-  // one 16-byte word per thread and parent: more threads with fewer stores in
-  // flight each measured faster than 2, 4 or 8 words per thread
+  // one 16-byte word per thread and parent, 256 threads per workgroup: more
+  // threads with fewer stores in flight each measured faster than 2, 4 or 8
+  // words per thread, and than workgroups of 512 or 1024 threads
   constexpr int NP = 1;
   const int64_t tiles = (a.words + (int64_t)kK3Threads * NP - 1) / ((int64_t)kK3Threads * NP);
   (void)tiles_per_row;
