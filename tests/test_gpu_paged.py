@@ -146,6 +146,16 @@ def test_w16_paged(dev):
     assert t == 20 and copies > 0
 
 
+def test_paged_12_byte_positions(dev):
+    # one KV head of 3 fp32 per position: the copies move 4-byte words
+    wl = synth.WORKLOADS["toy"].replace(batch=3, beam=4, vocab=40, max_steps=14, eos_id=-1,
+                                        stop="never", lp="none", alpha=0.0, seed=23,
+                                        kv_heads=1, head_dim=3)
+    assert wl.kv_bytes_per_pos == 12
+    rep, copies, t = run_paged(wl, 14, dev, 3, kv_planes=3)
+    assert t == 14 and copies > 0
+
+
 def test_w1_paged_never_copies(dev):
     wl = synth.WORKLOADS["toy"].replace(batch=2, beam=1, vocab=50, max_steps=9, eos_id=-1,
                                         stop="never", seed=3)

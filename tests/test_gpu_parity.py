@@ -468,6 +468,61 @@ PATTERNS = {
 }
 
 
+# (int32 words per position, padding words after each position, shared prompt
+# positions P before the generated ones, planes): 4-byte words (12-byte
+# positions) and 16-byte words, contiguous and padded positions, a prompt
+# region that must stay untouched, and more planes than one launch takes
+KV_LAYOUTS = {
+    "w4_contig": (3, 0, 0, 2),
+    "w4_padded": (3, 1, 0, 2),
+    "w16_padded": (8, 4, 0, 2),
+    "w16_prompt": (8, 0, 5, 2),
+    "w4_padded_prompt": (3, 2, 3, 3),
+    "w16_130_planes": (4, 0, 0, 130),
+}
+
+
+@pytest.mark.parametrize("W", [3, 16])
+@pytest.mark.parametrize("layout", sorted(KV_LAYOUTS))
+def test_kv_reorder_layouts(dev, layout, W):
+    """The reorder of positions [P, P + t) of every (layer, K|V) plane, for
+    the layouts a caller's cache may have, against the oracle's gather; the
+    padding between positions and the prompt positions are never written."""
+    import beam_search_step_amd as bs
+    words, pad, P, n_planes = KV_LAYOUTS[layout]
+    B, V, T = 3, 40, 7
+    rows = B * W
+    wl = synth.WORKLOADS["toy"].replace(batch=B, beam=W, vocab=V, eos_id=-1, stop="never",
+                                        lp="none", alpha=0.0, max_steps=T, seed=70 + W)
+    g = bs.BeamSearch.for_workload(wl)
+    ref = oracle.Search.for_workload(wl)
+    rng = np.random.default_rng(words * 100 + pad * 10 + P + W)
+    full0 = [rng.integers(-2 ** 31, 2 ** 31 - 1, size=(rows, P + T, words + pad), dtype=np.int64)
+             .astype(np.int32) for _ in range(n_planes)]
+    full = [torch.from_numpy(f).to(dev) for f in full0]
+    desc = bs.make_kv_desc([f[:, :, :words] for f in full], pos_offset=P)
+    host = [np.ascontiguousarray(f[:, :, :words]) for f in full0]
+    for t in range(1, T + 1):
+        lg = synth.logits(wl, t)
+        bi, tk, sc, dn = g.step(to_device(lg, dev))
+        obi, otk, osc, odn = ref.step(lg)
+        assert np.array_equal(bi.cpu().numpy(), obi) and np.array_equal(dn.cpu().numpy() != 0, odn)
+        # position P + t - 1 of every row gets fresh values before the reorder
+        for f, h in zip(full, host):
+            vals = rng.integers(-2 ** 31, 2 ** 31 - 1, size=(rows, words), dtype=np.int64) \
+                .astype(np.int32)
+            f[:, P + t - 1, :words] = torch.from_numpy(vals).to(dev)
+            h[:, P + t - 1] = vals
+        g.reorder_kv(desc, t)
+        oracle.kv_reorder(host, obi, odn, t, pos_offset=P)
+        for li, (f, h, f0) in enumerate(zip(full, host, full0)):
+            got = f.cpu().numpy()
+            assert np.array_equal(got[:, :, :words], h), f"{layout} W={W} t={t} plane {li}"
+            assert np.array_equal(got[:, :, words:], f0[:, :, words:]), \
+                f"{layout} W={W} t={t} plane {li}: padding written"
+    g.close()
+
+
 @pytest.mark.parametrize("name", sorted(PATTERNS))
 def test_kv_reorder_patterns(dev, name):
     import beam_search_step_amd as bs
