@@ -138,14 +138,27 @@ def test_llama3_8b_with_reachable_eos(dev):
     g.close()
 
 
-@pytest.mark.parametrize("tile_elems", [0, 16])
+@pytest.mark.parametrize("tile_elems", [0, 16, 32])
 def test_wide_beam_sampled_items(dev, tile_elems):
     """B=16, W=16, V=250000 fp32 (top-16 of 4.0M per item), 3 steps, items 3
     and 12. tile_elems=16 gives 62 tiles per row, so the merge runs in several
-    batches."""
+    batches; 32 gives 31 tiles of 8192 logits."""
     wl = synth.WORKLOADS["wide"]
     rep, g, ref = run_stepwise(wl, 3, dev, items=[3, 12], kv_planes=1, tile_elems=tile_elems)
     log(f"wide tile={tile_elems}: {rep}")
+    g.close()
+
+
+@pytest.mark.parametrize("W,V", [(4, 1001), (2, 4099), (8, 3000), (16, 20003)])
+def test_bf16_shapes(dev, W, V):
+    """bf16 logits whose rows are not 16-byte aligned (odd V: scalar loads)
+    and aligned rows with a ragged last tile, with EOS reachable."""
+    wl = synth.WORKLOADS["toy"].replace(batch=3, beam=W, vocab=V, dtype="bf16", sigma=3.0,
+                                        eos_id=3, eos_in_zipf=False, eos_ramp=4.0, ramp_steps=4,
+                                        lp="gnmt", alpha=0.6, max_steps=8, seed=90 + W,
+                                        num_return=min(W, 2), name=f"bf16_{W}_{V}")
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1)
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"bf16 W={W} V={V}")
     g.close()
 
 
