@@ -149,16 +149,20 @@ def test_wide_beam_sampled_items(dev, tile_elems):
     g.close()
 
 
-@pytest.mark.parametrize("W,V", [(4, 1001), (2, 4099), (8, 3000), (16, 20003)])
-def test_bf16_shapes(dev, W, V):
+@pytest.mark.parametrize("W,V,select,prune", [
+    (4, 1001, "fused", "topw"), (2, 4099, "fused", "topw"), (8, 3000, "fused", "topw"),
+    (16, 20003, "fused", "topw"), (4, 1001, "two_pass", "topw"), (4, 1001, "fused", "top2w"),
+    (2, 4099, "two_pass", "top2w")])
+def test_bf16_shapes(dev, W, V, select, prune):
     """bf16 logits whose rows are not 16-byte aligned (odd V: scalar loads)
-    and aligned rows with a ragged last tile, with EOS reachable."""
+    and aligned rows with a ragged last tile, with EOS reachable; also through
+    the two-pass selection and the 2W-candidate fill."""
     wl = synth.WORKLOADS["toy"].replace(batch=3, beam=W, vocab=V, dtype="bf16", sigma=3.0,
                                         eos_id=3, eos_in_zipf=False, eos_ramp=4.0, ramp_steps=4,
                                         lp="gnmt", alpha=0.6, max_steps=8, seed=90 + W,
                                         num_return=min(W, 2), name=f"bf16_{W}_{V}")
-    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1)
-    compare_final(g, ref, range(wl.batch), wl.num_return, f"bf16 W={W} V={V}")
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, kv_planes=1, select=select, prune=prune)
+    compare_final(g, ref, range(wl.batch), wl.num_return, f"bf16 W={W} V={V} {select} {prune}")
     g.close()
 
 
