@@ -214,7 +214,10 @@ def bench_search(args, torch, bs, dev):
         kv_b, logit_b = step_bytes(ts, bi, sc, dn)
         return kv_b, logit_b, int((~dn).sum())
 
+    kv_rw = [0, 0]  # KV bytes read (distinct parents) and written (moved slots)
+
     def step_bytes(ts, bi, sc, dn):
+        kv_rw[0] = kv_rw[1] = 0
         kv_bytes = []
         logit_bytes = []
         prev_live = np.zeros((B, W), bool)
@@ -246,6 +249,8 @@ def bench_search(args, torch, bs, dev):
                     moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
                     parents = {int(bi[i, b, w]) for w in moved}
                     moved_total += len(moved) + len(parents)
+                    kv_rw[0] += len(parents) * t * bpp * planes_n
+                    kv_rw[1] += len(moved) * t * bpp * planes_n
                 kv_bytes.append(moved_total * t * bpp * planes_n)
             prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
         return np.array(kv_bytes, np.float64), np.array(logit_bytes, np.float64)
@@ -286,6 +291,7 @@ def bench_search(args, torch, bs, dev):
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
         "live_item_steps": live_item_steps,
+        **({} if paged else {"kv_read_write_bytes": list(kv_rw)}),
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if args.events:
