@@ -70,6 +70,9 @@ def parse(argv=None):
                     help="KV cache: contiguous rows (bs_reorder_kv) or block tables with copy "
                          "on write (bs_kv_paged_reorder)")
     ap.add_argument("--block-size", type=int, default=16, help="positions per block (--kv paged)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="batch items (0: the workload's); e.g. one GPU's share when the batch "
+                         "is split over GPUs")
     ap.add_argument("--pool", type=int, default=0, help="logit buffers (0: per workload)")
     ap.add_argument("--distinct", type=int, default=0, help="distinct steps (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -109,12 +112,16 @@ def bench_search(args, torch, bs, dev):
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.batch:
+        wl = wl.replace(batch=args.batch)
     B, W, V, T = wl.batch, wl.beam, wl.vocab, wl.max_steps
     planes_n = 2 * wl.layers
     bpp = wl.kv_bytes_per_pos
     if wl.name == "llama3_8b":
         assert W * V == 513024 and wl.kv_bytes_per_token == 131072
     pool_n, distinct_n = POOLS[wl.name]
+    # at any batch, enough buffers for twice the 256 MB Infinity Cache
+    pool_n = max(pool_n, -(-512_000_000 // (wl.rows * V * wl.elem_bytes)))
     pool_n = args.pool or pool_n
     distinct_n = min(args.distinct or distinct_n, pool_n)
 
@@ -317,7 +324,10 @@ def bench_search(args, torch, bs, dev):
             out["roofline"] = {
                 "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": measured_traffic(wl.name),
+                # the counters were taken on the default run (top-W, the
+                # workload's own batch); other runs change the reorder's bytes
+                "traffic": measured_traffic(wl.name)
+                           if args.prune == "topw" and not args.batch else None,
                 "alg_bytes_per_launch": kv_bytes_ev.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
             }
         out["step_kernels"] = {
