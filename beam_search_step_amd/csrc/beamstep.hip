@@ -353,6 +353,7 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   if (c.batch < 1 || c.beam < 1 || c.beam > kMaxBeam || c.vocab < 1 || c.max_steps < 1)
     return BS_EINVAL;
   if ((int64_t)c.beam * c.vocab >= ((int64_t)1 << 31)) return BS_EINVAL;
+  if ((int64_t)c.batch * c.beam > kMaxGridRows) return BS_EINVAL;
   if ((int64_t)c.batch * c.beam * c.max_steps >= ((int64_t)1 << 31)) return BS_EINVAL;
   if (c.logits_dtype != BS_F32 && c.logits_dtype != BS_BF16) return BS_EINVAL;
   if (c.lp < BS_LP_NONE || c.lp > BS_LP_POW) return BS_EINVAL;
@@ -797,6 +798,7 @@ int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dty
   if (!out) return BS_EINVAL;
   *out = nullptr;
   if (batch < 1 || k < 1 || k > 64 || vocab < 1) return BS_EINVAL;
+  if ((int64_t)batch * k > kMaxGridRows) return BS_EINVAL;
   if (logits_dtype != BS_F32 && logits_dtype != BS_BF16) return BS_EINVAL;
   bs_verify_state* h = (bs_verify_state*)calloc(1, sizeof(bs_verify_state));
   if (!h) return BS_ENOMEM;

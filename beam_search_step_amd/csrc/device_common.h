@@ -9,6 +9,7 @@ namespace {
 constexpr int kThreads = 256;           // workgroup size of K1, K2, K3, K4
 constexpr int kWaves = kThreads / 64;   // wave64
 constexpr int kMaxBeam = 16;
+constexpr int kMaxGridRows = 65535;     // rows per launch: the grid's y extent
 constexpr int kListCap = 1024;          // LDS candidate list of the top-W
 constexpr int kGroups = kThreads / 16;  // 16-lane groups for the selection bound
 constexpr int kMergeNE = 8;             // K2 candidates per thread per batch

@@ -94,7 +94,7 @@ typedef enum { BS_PRUNE_TOPW = 0, BS_PRUNE_TOP2W = 1 } bs_prune;
 typedef enum { BS_SELECT_FUSED = 0, BS_SELECT_TWO_PASS = 1 } bs_select;
 
 typedef struct {
-    int32_t batch;        /* B >= 1                                        */
+    int32_t batch;        /* B >= 1, with B*W <= 65535                     */
     int32_t beam;         /* W, 1..16                                      */
     int32_t vocab;        /* V >= 1, with W*V < 2^31                       */
     int32_t max_steps;    /* T >= 1: decode steps, the longest hypothesis  */
@@ -313,7 +313,8 @@ void bs_destroy(bs_state *h);
 typedef struct bs_verify_state bs_verify_state;
 
 /* Allocates the per-tile partial results for logits [B][k][V] once.
- *   batch >= 1, k in 1..64, vocab >= 1; logits_dtype a bs_dtype. */
+ *   batch >= 1, k in 1..64, batch*k <= 65535, vocab >= 1; logits_dtype a
+ *   bs_dtype. */
 int bs_verify_create(int32_t batch, int32_t k, int32_t vocab, int32_t logits_dtype,
                      void *hip_stream, bs_verify_state **out);
 

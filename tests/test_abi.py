@@ -48,6 +48,7 @@ def _cfg(**kw):
     dict(batch=0), dict(beam=0), dict(beam=17), dict(vocab=0), dict(max_steps=0),
     dict(logits_dtype=2), dict(lp=3), dict(stop=3), dict(num_return=0), dict(num_return=5),
     dict(tile_elems=8), dict(alpha=float("nan")), dict(beam=16, vocab=2 ** 27), dict(select=2),
+    dict(batch=16384, beam=4), dict(batch=65536, beam=1),
 ])
 def test_create_rejects_invalid_config(kw):
     h = ctypes.c_void_p(123)
@@ -67,6 +68,7 @@ def test_null_arguments_are_rejected():
     h = ctypes.c_void_p()
     assert L.bs_verify_create(0, 8, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
     assert L.bs_verify_create(2, 65, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
+    assert L.bs_verify_create(1025, 64, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
     assert L.bs_kv_paged_create(None, 16, 64, ctypes.byref(h)) == bs.BS_EINVAL
     assert L.bs_kv_paged_reset(None) == bs.BS_EINVAL
     assert L.bs_kv_paged_table(None, None, None) == bs.BS_EINVAL
