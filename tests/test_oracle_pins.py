@@ -533,3 +533,26 @@ def test_top2w_without_eos_equals_topw(orc, seed):
 def test_top2w_rejects_bad_mode(orc):
     with pytest.raises(ValueError):
         orc.Search(1, 2, 3, 2, prune="top3w")
+
+
+def test_verify_workload_acceptance_rate(orc):
+    """The verify workload's acceptance structure, through the oracle's prefix
+    rule: position 0 always matches and each later position matches with
+    probability 0.6, independently, so the accepted block k^ = 1 + (number of
+    leading matches among positions 1..7) has P(k^ = m) = 0.6^(m-1) * 0.4 for
+    m < 8, P(k^ = 8) = 0.6^7 and mean 1 + sum_{m=1..7} 0.6^m = 2.458. The
+    sample is 40 seeded calls of 64 items (2560 blocks; the standard error of
+    the mean is about 0.035). A smaller vocabulary than the workload's 32000
+    leaves the acceptance unchanged: a non-planted position matches only if
+    its uniform proposal happens to be the argmax (1 in 2000)."""
+    p, k = 0.6, 8
+    mean_exact = 1 + sum(p ** m for m in range(1, k))
+    assert abs(mean_exact - 2.458) < 5e-4
+    acc = np.concatenate([orc.verify(*synth.verify_inputs(64, k, 2000, seed=1004, call=c))[0]
+                          for c in range(40)])
+    assert acc.min() >= 1 and acc.max() <= k
+    assert abs(acc.mean() - mean_exact) < 0.15, acc.mean()
+    # the shape of the distribution, not only its mean
+    freq = np.bincount(acc, minlength=k + 1)[1:] / acc.size
+    want = [p ** (m - 1) * (1 - p) for m in range(1, k)] + [p ** (k - 1)]
+    assert np.abs(freq - np.array(want)).max() < 0.04, (freq, want)
