@@ -325,9 +325,11 @@ def bench_search(args, torch, bs, dev):
                 "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                 # the counters were taken on the default run (top-W, the
-                # workload's own batch); other runs change the reorder's bytes
-                "traffic": measured_traffic(wl.name)
-                           if args.prune == "topw" and not args.batch else None,
+                # workload's own batch and logit pool); other runs change the
+                # reorder's bytes
+                "traffic": measured_traffic("k3_kv_reorder", wl.name, args.steps, T)
+                           if args.prune == "topw" and not (args.batch or args.pool
+                                                            or args.distinct) else None,
                 "alg_bytes_per_launch": kv_bytes_ev.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
             }
         out["step_kernels"] = {
@@ -421,7 +423,10 @@ def bench_verify(args, torch, bs, dev):
         ach = alg / d.mean() / 1e9
         out["roofline"] = {"bound": "hbm", "kernel": "k4_row (row segments) + k4_accept, one call",
                            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                           "frac": ach / PEAK_HBM_GBS,
+                           # counters taken on the exact criterion (one call
+                           # of either kind reads the same logits)
+                           "traffic": measured_traffic("k4_verify", "verify") if exact else None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
         out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     # model calls per generated token implied by the mean accepted block k^
@@ -472,29 +477,43 @@ def copy_reference(torch, dev):
     return {"bytes_read_plus_written": 2 * n, "avg_us": us, "GBs": 2 * n / us / 1e3}
 
 
-def k3_source_hash():
-    """Hash of the KV-reorder kernel's source (csrc/kv_reorder.h from its
-    section header on): counter readings are only used while the kernel they
-    were taken on is unchanged."""
+# kernels with a committed counter summary: the source file and the first line
+# of the kernel's section in it
+TRAFFIC_SOURCES = {"k3_kv_reorder": ("kv_reorder.h", "// K3: in-place KV reorder"),
+                   "k4_verify": ("verify.h", "// K4: blockwise verify")}
+
+
+def kernel_source_hash(kernel):
+    """Hash of a kernel's source (its csrc file from the kernel's section
+    header on): counter readings are only used while the kernel they were
+    taken on is unchanged."""
     import hashlib
-    src = open(os.path.join(ROOT, "beam_search_step_amd", "csrc", "kv_reorder.h")).read()
-    i = src.index("// K3: in-place KV reorder")
-    return hashlib.sha256(src[i:].encode()).hexdigest()[:16]
+    fname, marker = TRAFFIC_SOURCES[kernel]
+    src = open(os.path.join(ROOT, "beam_search_step_amd", "csrc", fname)).read()
+    return hashlib.sha256(src[src.index(marker):].encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per KV-reorder launch from the committed rocprofv3 counter
-    summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain
-    copy's reading), or None when there is none for the current kernel."""
-    path = os.path.join(ROOT, "profiles", f"k3_kv_reorder_{workload}_traffic.json")
+def measured_traffic(kernel, workload, steps=None, steps_per_search=None):
+    """HBM bytes per launch (per call, for verify) from the committed
+    rocprofv3 counter summary of this kernel and workload (FETCH_SIZE +
+    WRITE_SIZE, each scaled by a plain copy's reading), or None: when there is
+    none for the current kernel, or when this run's steps are not the counted
+    ones (a search's launches move more KV as t grows, so the mean per launch
+    depends on which steps were run; whole searches all have the same mean)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("k3_source_sha256_16") != k3_source_hash():
+    if d.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
-    return d.get("bytes_per_launch")
+    if steps_per_search is not None:
+        counted = d.get("steps")
+        whole = counted and steps % steps_per_search == 0 and counted % steps_per_search == 0
+        if steps != counted and not whole:
+            return None
+    return d.get("bytes_per_launch", d.get("bytes_per_call"))
 
 
 def pin_one_core():

@@ -42,3 +42,34 @@ def test_bench_line(capsys, workload):
     assert "traffic" in r
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
+
+
+def test_traffic_summaries_are_consistent():
+    """Every committed counter summary: the bytes it reports are its two
+    counters scaled by the plain-copy calibration of the same runs, and
+    bench.py finds it while the kernel it was taken on is unchanged."""
+    import glob
+    sys.path.insert(0, ROOT)
+    import bench
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")))
+    assert len(paths) >= 4
+    for p in paths:
+        with open(p) as f:
+            d = json.load(f)
+        cal = d["calibration"]
+        assert abs(cal["fetch_factor"] * cal["fetch_kib_per_dispatch"] * 1024 - cal["bytes_read"]) \
+            < 1e-3 * cal["bytes_read"]
+        assert abs(cal["write_factor"] * cal["write_kib_per_dispatch"] * 1024 - cal["bytes_written"]) \
+            < 1e-3 * cal["bytes_written"]
+        parts = d.get("per_kernel", {"": d})
+        total = sum(1024 * (k["fetch_kib_per_dispatch"] * cal["fetch_factor"]
+                            + k["write_kib_per_dispatch"] * cal["write_factor"])
+                    for k in parts.values())
+        got = d.get("bytes_per_launch", d.get("bytes_per_call"))
+        assert abs(total - got) < 1e-4 * got, p
+        assert all("bench.py" in c for c in d["commands"])
+        stem = os.path.basename(p)[:-len("_traffic.json")]
+        kernel = next(k for k in bench.TRAFFIC_SOURCES if stem.startswith(k + "_"))
+        workload = stem[len(kernel) + 1:]
+        per_search = None if kernel == "k4_verify" else d["steps"]
+        assert bench.measured_traffic(kernel, workload, d["steps"], per_search) == got, p
