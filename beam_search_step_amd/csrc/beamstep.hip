@@ -210,25 +210,29 @@ void launch_k2(const K2Args& a, int wmax, hipStream_t s) {
 }
 
 // ---- K3 dispatch ----------------------------------------------------------
+// one 16-byte word per thread and parent, 256 threads per workgroup: more
+// threads with fewer stores in flight each measured faster than 2, 4 or 8
+// words per thread, and than workgroups of 512 or 1024 threads
+constexpr int kK3Words = 1;
+// workgroups along a row: the grid's x extent times the workgroup size must
+// stay below 2^32 work-items
+constexpr int64_t kK3MaxTiles = 0xFFFFFFFFll / kK3Threads;
+
 template <int WMAX, int WORD, bool CONTIG>
-void launch_k3_c(const K3Args& a, int64_t tiles_per_row, int B, int nplanes, hipStream_t s) {
-  // one 16-byte word per thread and parent, 256 threads per workgroup: more
-  // threads with fewer stores in flight each measured faster than 2, 4 or 8
-  // words per thread, and than workgroups of 512 or 1024 threads
-  constexpr int NP = 1;
+void launch_k3_c(const K3Args& a, int B, int nplanes, hipStream_t s) {
+  constexpr int NP = kK3Words;
   const int64_t tiles = (a.words + (int64_t)kK3Threads * NP - 1) / ((int64_t)kK3Threads * NP);
-  (void)tiles_per_row;
   dim3 g((unsigned)tiles, B, nplanes);
   hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, a);
 }
 template <int WMAX>
 void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s) {
   if (word == 16) {
-    if (contig) launch_k3_c<WMAX, 16, true>(a, 0, B, nplanes, s);
-    else launch_k3_c<WMAX, 16, false>(a, 0, B, nplanes, s);
+    if (contig) launch_k3_c<WMAX, 16, true>(a, B, nplanes, s);
+    else launch_k3_c<WMAX, 16, false>(a, B, nplanes, s);
   } else {
-    if (contig) launch_k3_c<WMAX, 4, true>(a, 0, B, nplanes, s);
-    else launch_k3_c<WMAX, 4, false>(a, 0, B, nplanes, s);
+    if (contig) launch_k3_c<WMAX, 4, true>(a, B, nplanes, s);
+    else launch_k3_c<WMAX, 4, false>(a, B, nplanes, s);
   }
 }
 void launch_k3(const K3Args& a, int wmax, int word, bool contig, int B, int nplanes,
@@ -361,7 +365,7 @@ int bs_create(const bs_config* cfg, void* hip_stream, bs_state** out) {
   if (c.num_return < 1 || c.num_return > c.beam) return BS_EINVAL;
   if (c.tile_elems != 0 && c.tile_elems != 16 && c.tile_elems != 32 && c.tile_elems != 64)
     return BS_EINVAL;
-  if (!(c.alpha == c.alpha)) return BS_EINVAL;
+  if (!isfinite(c.alpha)) return BS_EINVAL;
   if (c.prune != BS_PRUNE_TOPW && c.prune != BS_PRUNE_TOP2W) return BS_EINVAL;
   if (c.prune == BS_PRUNE_TOP2W && 2 * c.beam > kMaxBeam) return BS_EINVAL;
   if (c.select != BS_SELECT_FUSED && c.select != BS_SELECT_TWO_PASS) return BS_EINVAL;
@@ -569,6 +573,8 @@ int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
   a.base_off = base_off;
   a.words_per_pos = kv->bytes_per_pos / word;
   a.words = (int64_t)gen_len * a.words_per_pos;
+  if ((a.words + kK3Threads * kK3Words - 1) / (kK3Threads * kK3Words) > kK3MaxTiles)
+    return BS_EINVAL;
   a.W = h->W;
   a.plan = h->st.plan;
   for (int p0 = 0; p0 < kv->n_planes; p0 += kMaxPlanesPerLaunch) {

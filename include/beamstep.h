@@ -102,7 +102,7 @@ typedef struct {
     int32_t pad_id;       /* token reported for dead slots and padding     */
     int32_t logits_dtype; /* bs_dtype                                      */
     int32_t lp;           /* bs_lp                                         */
-    double alpha;         /* length-penalty exponent                       */
+    double alpha;         /* length-penalty exponent, finite               */
     int32_t stop;         /* bs_stop                                       */
     int32_t num_return;   /* hypotheses returned per item, 1..W            */
     int32_t tile_elems;   /* logits per thread in the streaming pass:
@@ -185,8 +185,13 @@ typedef struct {
  * for swaps and cycles.
  *   kv       host descriptor; planes are device pointers
  *   gen_len  number of positions to move (>= 0; 0 is a no-op)
+ * Each plane goes through one call per step: a second call on the same plane
+ * applies the step's permutation again. Planes may be split over several calls
+ * (different layouts, more planes than one launch takes).
  * Requires bytes_per_pos, row_stride, pos_stride, pos_offset*pos_stride and
- * every plane address to be multiples of 4 bytes (16 for the fast path).
+ * every plane address to be multiples of 4 bytes (16 for the fast path), and
+ * a row's gen_len * bytes_per_pos to be under 2^32 copy words (of 16 bytes on
+ * the fast path, 4 otherwise).
  * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
 int bs_reorder_kv(bs_state *h, const bs_kv_desc *kv, int32_t gen_len);
 

@@ -47,7 +47,7 @@ def _cfg(**kw):
 @pytest.mark.parametrize("kw", [
     dict(batch=0), dict(beam=0), dict(beam=17), dict(vocab=0), dict(max_steps=0),
     dict(logits_dtype=2), dict(lp=3), dict(stop=3), dict(num_return=0), dict(num_return=5),
-    dict(tile_elems=8), dict(alpha=float("nan")), dict(beam=16, vocab=2 ** 27), dict(select=2),
+    dict(tile_elems=8), dict(alpha=float("nan")), dict(alpha=float("inf")), dict(beam=16, vocab=2 ** 27), dict(select=2),
     dict(batch=16384, beam=4), dict(batch=65536, beam=1),
 ])
 def test_create_rejects_invalid_config(kw):

@@ -7,6 +7,7 @@ each step (teacher-forced, see tests/parity.py), final hypotheses, and the KV
 cache bit for bit. Sizes: the toy workload in full; the other workloads at
 their full B, W and V with a sample of batch items followed by the oracle.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -430,6 +431,13 @@ def test_error_paths_on_device(dev):
     with pytest.raises(bs.BeamStepError) as e:   # 2-byte positions: not a multiple of 4
         g.reorder_kv([torch.zeros((4, 3, 1), dtype=torch.int16, device=dev)], 1)
     assert e.value.status == bs.BS_EINVAL
+    # a row span of 2^32 sixteen-byte words would overflow the grid: rejected
+    # on the host, before any launch
+    plane = torch.zeros((4, 16), dtype=torch.int32, device=dev)
+    big = bs.make_kv_desc([plane.view(4, 1, 16)])
+    big.bytes_per_pos = big.pos_stride = 1 << 36
+    big.row_stride = 1 << 36
+    assert bs.library().bs_reorder_kv(g.h, ctypes.byref(big), 1) == bs.BS_EINVAL
     assert g.steps == 1
     g.reset()
     assert g.steps == 0
