@@ -223,7 +223,9 @@ void launch_k3_c(const K3Args& a, int B, int nplanes, hipStream_t s) {
   constexpr int NP = kK3Words;
   const int64_t tiles = (a.words + (int64_t)kK3Threads * NP - 1) / ((int64_t)kK3Threads * NP);
   dim3 g((unsigned)tiles, B, nplanes);
-  hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, a);
+  K3Args b = a;
+  b.whole_planes = nplanes % 8 == 0 && tiles * B * nplanes < 0xFFFFFFFFll;
+  hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, b);
 }
 template <int WMAX>
 void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s) {

@@ -18,6 +18,7 @@ struct K3Args {
   int64_t words_per_pos;
   int W;
   const int* plan;
+  int whole_planes;     // 1: XCD i takes the i-th eighth of the planes
 };
 
 template <int WORD>
@@ -80,10 +81,31 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
   }
 }
 
+// Work order. The hardware hands consecutive workgroups (x fastest, then y,
+// z) to the 8 XCDs in turn, so in grid order every XCD takes every eighth
+// tile of every row span. With whole_planes set (the launch's plane count a
+// multiple of 8, its workgroups fewer than 2^32), the workgroup that XCD i
+// receives k-th does the k-th workgroup of the i-th eighth of the grid
+// instead: XCD i streams planes [i*planes/8, (i+1)*planes/8) from end to end,
+// all items of each, and every XCD still gets the same share of every item.
+// Measured 1.3% faster than grid order with 64 planes of 8 items; an eighth
+// that does not end on a plane boundary lets some XCDs take most of the
+// heavy or unfinished items, and was slower (12 planes: 1.5% with 16 items,
+// 9% when many items had finished).
 template <int WMAX, int WORD, int NP, bool CONTIG>
 __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
   using WT = typename Word<WORD>::type;
-  const int b = blockIdx.y;
+  uint32_t bx = blockIdx.x, b = blockIdx.y, bz = blockIdx.z;
+  if (a.whole_planes) {
+    const uint32_t gx = gridDim.x, gy = gridDim.y;
+    const uint32_t lin = bx + gx * (b + gy * bz);
+    const uint32_t eighth = (gx * gy * gridDim.z) >> 3;
+    const uint32_t l2 = (lin & 7) * eighth + (lin >> 3);
+    const uint32_t pl = l2 / gx;
+    bx = l2 - pl * gx;
+    bz = pl / gy;
+    b = pl - bz * gy;
+  }
   const int* plan = a.plan + b * kPlanStride;
   // the whole plan is read up front, in one batch of scalar loads: a plan read
   // after a store would be a vector load whose wait also waits for every
@@ -97,13 +119,13 @@ __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
     dmask[q] = q < nsrc ? m0 : 0;
   }
   if (ndst == 0) return;
-  char* base = a.planes[blockIdx.z] + a.base_off;
+  char* base = a.planes[bz] + a.base_off;
   const int64_t row0 = (int64_t)b * a.W;
 
   int64_t off[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
-    const int64_t e = ((int64_t)blockIdx.x * NP + k) * kK3Threads + threadIdx.x;
+    const int64_t e = ((int64_t)bx * NP + k) * kK3Threads + threadIdx.x;
     if (CONTIG) {
       off[k] = e * WORD;
     } else {
@@ -112,8 +134,8 @@ __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
     }
   }
   // every word of the tile is in range (uniform), except in the last tile
-  const int64_t e0 = (int64_t)blockIdx.x * NP * kK3Threads + threadIdx.x;
-  if ((int64_t)(blockIdx.x + 1) * NP * kK3Threads <= a.words)
+  const int64_t e0 = (int64_t)bx * NP * kK3Threads + threadIdx.x;
+  if ((int64_t)(bx + 1) * NP * kK3Threads <= a.words)
     move_words<WMAX, WT, NP, true>(base, row0, a.row_stride, off, e0, a.words, nsrc, src, dmask);
   else
     move_words<WMAX, WT, NP, false>(base, row0, a.row_stride, off, e0, a.words, nsrc, src,

@@ -47,7 +47,8 @@ def test_bench_line(capsys, workload):
 def test_traffic_summaries_are_consistent():
     """Every committed counter summary: the bytes it reports are its two
     counters scaled by the plain-copy calibration of the same runs, and
-    bench.py finds it while the kernel it was taken on is unchanged."""
+    bench.py reports it exactly while the kernel it was taken on is
+    unchanged."""
     import glob
     sys.path.insert(0, ROOT)
     import bench
@@ -72,4 +73,7 @@ def test_traffic_summaries_are_consistent():
         kernel = next(k for k in bench.TRAFFIC_SOURCES if stem.startswith(k + "_"))
         workload = stem[len(kernel) + 1:]
         per_search = None if kernel == "k4_verify" else d["steps"]
-        assert bench.measured_traffic(kernel, workload, d["steps"], per_search) == got, p
+        found = bench.measured_traffic(kernel, workload, d["steps"], per_search)
+        # a summary taken on an earlier version of the kernel is not reported
+        current = d["source_sha256_16"] == bench.kernel_source_hash(kernel)
+        assert found == (got if current else None), p
