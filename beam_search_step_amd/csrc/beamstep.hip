@@ -83,12 +83,14 @@ struct bs_state {
   float* qc;
   int* qj;
   int* qn;
+  bs_kv_paged* paged;   // the paged cache whose table update bs_step runs
 };
 
 struct bs_kv_paged {
   bs_state* h;
   int bs, bpi, mb;
-  int last_t;  // the step last reordered (0: none since the reset)
+  int last_t;   // the step last reordered (0: none since the reset)
+  int table_t;  // the step whose table update has run (0: none since the reset)
   void* block;
   PagedDev pg;
 };
@@ -183,13 +185,22 @@ void launch_l3_t(const L3Args& a, int wmax, hipStream_t s) {
   }
 }
 
-void launch_k2(const K2Args& a, int wmax, hipStream_t s) {
+// K2 can run the paged cache's table update of the step in the same launch
+// (k2_select_finalize_paged) when rows have at most 64 tiles
+bool k2_fuses_paged(int tiles) { return tiles <= 64; }
+
+void launch_k2(const K2Args& a, int wmax, hipStream_t s, const K6Args* paged = nullptr) {
   dim3 g(a.B), blk(kThreads);
   if (a.tiles <= 64) {
     const int H = a.tiles <= 16 ? 1 : (a.tiles <= 32 ? 2 : 4);  // tiles per lane
     switch (wmax * 8 + H) {
-#define K2SEL(WM, HH) \
-  case WM * 8 + HH: hipLaunchKernelGGL((k2_select_finalize<WM, HH>), g, blk, 0, s, a); break;
+#define K2SEL(WM, HH)                                                                      \
+  case WM * 8 + HH:                                                                        \
+    if (paged)                                                                             \
+      hipLaunchKernelGGL((k2_select_finalize_paged<WM, HH>), g, blk, 0, s, a, *paged);     \
+    else                                                                                   \
+      hipLaunchKernelGGL((k2_select_finalize<WM, HH>), g, blk, 0, s, a);                   \
+    break;
       K2SEL(1, 1) K2SEL(1, 2) K2SEL(1, 4)
       K2SEL(2, 1) K2SEL(2, 2) K2SEL(2, 4)
       K2SEL(4, 1) K2SEL(4, 2) K2SEL(4, 4)
@@ -290,6 +301,18 @@ void fill_k2_args(K2Args& a2, bs_state* h, int t, int32_t* beam_idx, int32_t* to
   a2.out_tok = token_id;
   a2.out_score = scores;
   a2.out_done = done;
+}
+
+void fill_k6_args(K6Args& a6, const bs_kv_paged* p, const bs_state* h, int t) {
+  a6.pg = p->pg;
+  a6.s = h->st.s;
+  a6.done = h->st.done;
+  a6.plan = h->st.plan;
+  a6.W = h->W;
+  a6.bs = p->bs;
+  a6.bpi = p->bpi;
+  a6.mb = p->mb;
+  a6.t = t;
 }
 
 constexpr int kRowVerifyMinRows = 256;
@@ -543,9 +566,17 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
 
   K2Args a2;
   fill_k2_args(a2, h, t, beam_idx, token_id, scores, done);
-  launch_k2(a2, h->kmax, h->stream);
+  // the handle's paged cache, when every earlier step of the search has been
+  // reordered: K2 also runs this step's table update, and the reorder call
+  // only copies
+  bs_kv_paged* p = h->paged;
+  const bool fuse = p && k2_fuses_paged(h->tiles) && p->last_t == h->t && p->table_t == h->t;
+  K6Args a6;
+  if (fuse) fill_k6_args(a6, p, h, t);
+  launch_k2(a2, h->kmax, h->stream, fuse ? &a6 : nullptr);
   rc = launch_status();
   if (rc != BS_OK) return rc;
+  if (fuse) p->table_t = t;
   h->t = t;
   return BS_OK;
 }
@@ -643,6 +674,7 @@ int bs_kv_paged_create(bs_state* h, int32_t block_size, int32_t blocks_per_item,
     free(p);
     return rc;
   }
+  if (!h->paged) h->paged = p;  // the first cache of a handle: bs_step runs its table update
   *out = p;
   return BS_OK;
 }
@@ -652,7 +684,7 @@ int bs_kv_paged_reset(bs_kv_paged* p) {
   hipLaunchKernelGGL(k6_paged_init, dim3(p->h->B), dim3(kThreads), 0, p->h->stream, p->pg,
                      p->h->B, p->h->W, p->bpi, p->mb);
   const int rc = launch_status();
-  if (rc == BS_OK) p->last_t = 0;
+  if (rc == BS_OK) p->last_t = p->table_t = 0;
   return rc;
 }
 
@@ -684,19 +716,15 @@ int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len)
     a4 = a4 && ((uintptr_t)pool->pools[i] % 4 == 0);
   }
   if (!a4) return BS_EINVAL;
-  K6Args a6;
-  a6.pg = p->pg;
-  a6.s = h->st.s;
-  a6.done = h->st.done;
-  a6.plan = h->st.plan;
-  a6.W = h->W;
-  a6.bs = p->bs;
-  a6.bpi = p->bpi;
-  a6.mb = p->mb;
-  a6.t = gen_len;
-  hipLaunchKernelGGL(k6_paged_reorder, dim3(h->B), dim3(kThreads), 0, h->stream, a6);
-  int rc = launch_status();
-  if (rc != BS_OK) return rc;
+  int rc = BS_OK;
+  if (p->table_t != h->t) {  // bs_step did not run the table update of this step
+    K6Args a6;
+    fill_k6_args(a6, p, h, gen_len);
+    hipLaunchKernelGGL(k6_paged_reorder, dim3(h->B), dim3(kThreads), 0, h->stream, a6);
+    rc = launch_status();
+    if (rc != BS_OK) return rc;
+    p->table_t = h->t;
+  }
   const int word = a16 ? 16 : 4;
   K7Args a7;
   a7.block_stride = pool->block_stride;
@@ -742,6 +770,7 @@ int bs_kv_paged_status(bs_kv_paged* p, int32_t* overflow, int32_t* free_blocks) 
 
 void bs_kv_paged_destroy(bs_kv_paged* p) {
   if (!p) return;
+  if (p->h->paged == p) p->h->paged = nullptr;
   (void)hipStreamSynchronize(p->h->stream);
   (void)hipFree(p->block);
   free(p);

@@ -659,7 +659,7 @@ __device__ __forceinline__ float row16_sum_f(float v) {
 // w's list; a lower row means a lower flat index), and the K winners are put
 // in exact (score desc, flat index asc) order before the finalize.
 template <int WMAX, int H>
-__global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
+__device__ __forceinline__ void select_finalize_item(const K2Args& a) {
   __shared__ HypSmem<WMAX> hy;
   __shared__ float row_sc[kMaxBeam][WMAX];  // each row's best K, merge order
   __shared__ int row_j[kMaxBeam][WMAX];
@@ -852,6 +852,11 @@ __global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const uint64_t key = lane < K ? ordered[lane] : 0;
   finalize_item<WMAX>(a, hy, plan, b, lane, key, lp_t, lp_T);
+}
+
+template <int WMAX, int H>
+__global__ __launch_bounds__(kThreads) void k2_select_finalize(K2Args a) {
+  select_finalize_item<WMAX, H>(a);
 }
 
 }  // namespace

@@ -223,6 +223,14 @@ typedef struct {
  * the table [B*W][max_blocks] with max_blocks = T / block_size + 1 (blocks
  * for positions 0..T), and per item blocks_per_item reference counts and a
  * free list. Then resets them as bs_kv_paged_reset does. Synchronises.
+ * The first cache created on a handle is attached to it: while every step of
+ * the search has been reordered, in order, bs_step runs the table part of
+ * the next reorder (see bs_kv_paged_reorder) in its own launch when it uses
+ * the fused selection and a row spans at most 64 tiles of its streaming pass
+ * (V <= 64 * 256 * the logits per thread, tile_elems or the library's
+ * choice), and bs_kv_paged_reorder then only makes the copies. The table
+ * therefore shows step t's blocks from that bs_step on. Destroy a cache
+ * before its handle.
  *   block_size       positions per block, >= 1
  *   blocks_per_item  W <= blocks_per_item <= 4096; W * max_blocks always
  *                    suffices, fewer relies on shared prefixes
@@ -254,7 +262,9 @@ int bs_kv_paged_table(const bs_kv_paged *p, int32_t **table, int32_t *max_blocks
  *      slot but the lowest gets a private copy of that block's first
  *      t % block_size positions in every pool (the copy on write).
  * Afterwards every live row's positions [0, t), read through the table, hold
- * what its parent's held before the call, bit for bit.
+ * what its parent's held before the call, bit for bit. For the cache attached
+ * to the handle, (1) and the block assignment of (2) may already have run in
+ * bs_step (see bs_kv_paged_create); the result after this call is the same.
  *   pool     host descriptor of the caller's pools; block_stride, pos_stride,
  *            bytes_per_pos and every pool address must be multiples of 4 bytes
  *            (16 for the fast path)

@@ -35,16 +35,23 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits_fn=None):
+def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits_fn=None,
+              select="fused", second_cache=False):
     """Teacher-forced search of ``steps`` steps with a paged cache of
-    ``kv_planes`` pools; returns (Report, copies made, steps run)."""
+    ``kv_planes`` pools; returns (Report, copies made, steps run).
+
+    With the fused selection the step's table update runs inside bs_step for
+    the first cache of a handle; with the two-pass selection, or for a second
+    cache of the same handle (``second_cache``: another cache is created first
+    and never reordered), the reorder call launches it."""
     import beam_search_step_amd as bs
 
     logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     rep = Report()
     B, W = wl.batch, wl.beam
-    gpu = bs.BeamSearch.for_workload(wl)
+    gpu = bs.BeamSearch.for_workload(wl, select=select)
     ref = oracle.Search.for_workload(wl)
+    first = bs.PagedKV(gpu, block_size, blocks_per_item) if second_cache else None
     pk = bs.PagedKV(gpu, block_size, blocks_per_item)
     bpi = pk.blocks_per_item
     words = wl.kv_bytes_per_pos // 4
@@ -113,6 +120,8 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
         if odn.all():
             break
     pk.close()
+    if first is not None:
+        first.close()
     gpu.close()
     return rep, copies, t_run
 
@@ -122,6 +131,16 @@ def test_toy_paged(dev, block_size):
     wl = synth.WORKLOADS["toy"]
     rep, copies, t = run_paged(wl, wl.max_steps, dev, block_size)
     log(f"toy bs={block_size}: {t} steps, {copies} copies, {rep}")
+
+
+@pytest.mark.parametrize("how", ["two_pass", "second_cache"])
+def test_paged_update_by_the_reorder_call(dev, how):
+    # the table update launched by bs_kv_paged_reorder instead of bs_step
+    wl = synth.WORKLOADS["toy"].replace(batch=3, beam=4, vocab=40, max_steps=16, eos_id=-1,
+                                        stop="never", lp="none", alpha=0.0, seed=29)
+    kw = dict(select="two_pass") if how == "two_pass" else dict(second_cache=True)
+    rep, copies, t = run_paged(wl, 16, dev, 3, kv_planes=2, **kw)
+    assert t == 16 and copies > 0
 
 
 @pytest.mark.parametrize("seed", [5, 11])
