@@ -180,6 +180,34 @@ def test_vocab_above_a_million(dev, select):
     g.close()
 
 
+def test_maximum_rows(dev):
+    """B*W = 65520 rows, near the 65535 the launch grids take (K1's y extent,
+    and the reorder's items): 4095 items of 16 beams over a 37-token
+    vocabulary with EOS, 4 steps with the KV reorder, items followed at both
+    ends and in the middle."""
+    wl = synth.WORKLOADS["toy"].replace(batch=4095, beam=16, vocab=37, max_steps=4, seed=71,
+                                        num_return=2, name="maxrows")
+    assert wl.rows == 65520
+    items = [0, 1, 2047, 4093, 4094]
+    rep, g, ref = run_stepwise(wl, 4, dev, items=items, kv_planes=1)
+    compare_final(g, ref, items, 2, "max rows")
+    g.close()
+    log(f"max rows: {rep}")
+
+
+def test_verify_maximum_rows(dev):
+    """B*k = 65528 verify rows (8191 items of 8 positions), V = 33: one row
+    kernel workgroup per row, every row compared with the oracle."""
+    import beam_search_step_amd as bs
+    lg, prop = synth.verify_inputs(8191, 8, 33, seed=77)
+    ver = bs.Verifier(8191, 8, 33)
+    acc, am = ver(torch.from_numpy(lg).to(dev), torch.from_numpy(prop).to(dev))
+    oacc, oam = oracle.verify(lg, prop)
+    assert np.array_equal(am.cpu().numpy(), oam)
+    assert np.array_equal(acc.cpu().numpy(), oacc)
+    ver.close()
+
+
 # ---------------------------------------------------------------------------
 # Hugging Face 2W-candidate variant
 # ---------------------------------------------------------------------------
