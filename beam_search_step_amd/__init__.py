@@ -80,6 +80,7 @@ def library() -> ctypes.CDLL:
         L.bs_reset.argtypes = [P]
         L.bs_step.argtypes = [P, P, i64, P, P, P, P]
         L.bs_reorder_kv.argtypes = [P, ctypes.POINTER(bs_kv_desc), i32]
+        L.bs_reorder_kv_timed.argtypes = [P, ctypes.POINTER(bs_kv_desc), i32, P, P]
         L.bs_finalize.argtypes = [P, P, P, P]
         L.bs_last_selection.argtypes = [P, P, P]
         L.bs_get_finished.argtypes = [P, P, P, P, P, P, P]
@@ -98,7 +99,8 @@ def library() -> ctypes.CDLL:
         L.bs_verify_ex.argtypes = [P, P, i64, P, i32, i32, P, P, P]
         L.bs_verify_destroy.argtypes = [P]
         L.bs_verify_destroy.restype = None
-        for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_finalize",
+        for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_reorder_kv_timed",
+                     "bs_finalize",
                      "bs_last_selection", "bs_get_finished", "bs_steps_taken",
                      "bs_kv_paged_create", "bs_kv_paged_reset", "bs_kv_paged_table",
                      "bs_kv_paged_reorder", "bs_kv_paged_status",
@@ -170,6 +172,14 @@ def make_kv_desc(planes: Sequence, pos_offset: int = 0) -> bs_kv_desc:
 
 def bs_reorder_kv(h: int, kv: bs_kv_desc, gen_len: int) -> None:
     _check(library().bs_reorder_kv(h, ctypes.byref(kv), gen_len), "bs_reorder_kv")
+
+
+def bs_reorder_kv_timed(h: int, kv: bs_kv_desc, gen_len: int, start_event: int,
+                        stop_event: int) -> None:
+    """bs_reorder_kv with hipEvent_t handles (ints, 0 for none) attached to
+    its first and last kernel dispatch."""
+    _check(library().bs_reorder_kv_timed(h, ctypes.byref(kv), gen_len, start_event or None,
+                                         stop_event or None), "bs_reorder_kv_timed")
 
 
 def bs_kv_paged_create(h: int, block_size: int, blocks_per_item: int) -> int:

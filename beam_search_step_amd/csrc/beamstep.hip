@@ -38,6 +38,7 @@
 // No matrix cores: nothing here is a dense contraction. Every kernel is bound
 // by HBM bandwidth or, at small shapes, by latency.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -229,33 +230,45 @@ constexpr int kK3Words = 1;
 // stay below 2^32 work-items
 constexpr int64_t kK3MaxTiles = 0xFFFFFFFFll / kK3Threads;
 
+// Timing events (either may be null) are attached to the dispatch itself
+// (hipExtLaunchKernel), so they take the kernel's own start and end and put
+// no separate record on the stream.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 template <int WMAX, int WORD, bool CONTIG>
-void launch_k3_c(const K3Args& a, int B, int nplanes, hipStream_t s) {
+void launch_k3_c(const K3Args& a, int B, int nplanes, hipStream_t s, LaunchEvents ev) {
   constexpr int NP = kK3Words;
   const int64_t tiles = (a.words + (int64_t)kK3Threads * NP - 1) / ((int64_t)kK3Threads * NP);
   dim3 g((unsigned)tiles, B, nplanes);
   K3Args b = a;
   b.whole_planes = nplanes % 8 == 0 && tiles * B * nplanes < 0xFFFFFFFFll;
-  hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, b);
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s,
+                          ev.start, ev.stop, 0, b);
+  else
+    hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, b);
 }
 template <int WMAX>
-void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s) {
+void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s,
+                 LaunchEvents ev) {
   if (word == 16) {
-    if (contig) launch_k3_c<WMAX, 16, true>(a, B, nplanes, s);
-    else launch_k3_c<WMAX, 16, false>(a, B, nplanes, s);
+    if (contig) launch_k3_c<WMAX, 16, true>(a, B, nplanes, s, ev);
+    else launch_k3_c<WMAX, 16, false>(a, B, nplanes, s, ev);
   } else {
-    if (contig) launch_k3_c<WMAX, 4, true>(a, B, nplanes, s);
-    else launch_k3_c<WMAX, 4, false>(a, B, nplanes, s);
+    if (contig) launch_k3_c<WMAX, 4, true>(a, B, nplanes, s, ev);
+    else launch_k3_c<WMAX, 4, false>(a, B, nplanes, s, ev);
   }
 }
 void launch_k3(const K3Args& a, int wmax, int word, bool contig, int B, int nplanes,
-               hipStream_t s) {
+               hipStream_t s, LaunchEvents ev) {
   switch (wmax) {
-    case 1: launch_k3_w<1>(a, word, contig, B, nplanes, s); break;
-    case 2: launch_k3_w<2>(a, word, contig, B, nplanes, s); break;
-    case 4: launch_k3_w<4>(a, word, contig, B, nplanes, s); break;
-    case 8: launch_k3_w<8>(a, word, contig, B, nplanes, s); break;
-    default: launch_k3_w<16>(a, word, contig, B, nplanes, s); break;
+    case 1: launch_k3_w<1>(a, word, contig, B, nplanes, s, ev); break;
+    case 2: launch_k3_w<2>(a, word, contig, B, nplanes, s, ev); break;
+    case 4: launch_k3_w<4>(a, word, contig, B, nplanes, s, ev); break;
+    case 8: launch_k3_w<8>(a, word, contig, B, nplanes, s, ev); break;
+    default: launch_k3_w<16>(a, word, contig, B, nplanes, s, ev); break;
   }
 }
 
@@ -581,12 +594,17 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   return BS_OK;
 }
 
-int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
+static int reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len, LaunchEvents ev) {
   if (!h || !kv || !kv->planes || kv->n_planes < 1 || gen_len < 0) return BS_EINVAL;
   if (kv->bytes_per_pos <= 0 || kv->row_stride <= 0 || kv->pos_stride <= 0 || kv->pos_offset < 0)
     return BS_EINVAL;
   if (h->t == 0) return BS_ESTATE;
-  if (gen_len == 0) return BS_OK;
+  if (gen_len == 0) {  // nothing to launch: the events are recorded back to back
+    if ((ev.start && hipEventRecord(ev.start, h->stream) != hipSuccess) ||
+        (ev.stop && hipEventRecord(ev.stop, h->stream) != hipSuccess))
+      return BS_EDEVICE;
+    return BS_OK;
+  }
   const int64_t base_off = kv->pos_offset * kv->pos_stride;
   bool a16 = (kv->bytes_per_pos % 16 == 0) && (kv->row_stride % 16 == 0) &&
              (kv->pos_stride % 16 == 0) && (base_off % 16 == 0);
@@ -614,11 +632,28 @@ int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
     const int np = kv->n_planes - p0 < kMaxPlanesPerLaunch ? kv->n_planes - p0
                                                            : kMaxPlanesPerLaunch;
     for (int i = 0; i < np; ++i) a.planes[i] = (char*)kv->planes[p0 + i];
-    launch_k3(a, h->wmax, word, contig, h->B, np, h->stream);
+    // the start event goes with the first launch of the call, the stop event
+    // with the last
+    LaunchEvents le;
+    le.start = p0 == 0 ? ev.start : nullptr;
+    le.stop = p0 + np == kv->n_planes ? ev.stop : nullptr;
+    launch_k3(a, h->wmax, word, contig, h->B, np, h->stream, le);
     const int rc = launch_status();
     if (rc != BS_OK) return rc;
   }
   return BS_OK;
+}
+
+int bs_reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len) {
+  return reorder_kv(h, kv, gen_len, LaunchEvents());
+}
+
+int bs_reorder_kv_timed(bs_state* h, const bs_kv_desc* kv, int32_t gen_len, void* start_event,
+                        void* stop_event) {
+  LaunchEvents ev;
+  ev.start = (hipEvent_t)start_event;
+  ev.stop = (hipEvent_t)stop_event;
+  return reorder_kv(h, kv, gen_len, ev);
 }
 
 int bs_kv_paged_create(bs_state* h, int32_t block_size, int32_t blocks_per_item,

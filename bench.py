@@ -78,8 +78,11 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline: time budget of its sample (steps run until it is spent)")
-    ap.add_argument("--events", type=int, default=1,
-                    help="record HIP events around each KV-reorder launch (roofline)")
+    ap.add_argument("--events", type=int, default=1, choices=[0, 1, 2],
+                    help="KV-reorder launch durations (roofline), from a second pass of the same "
+                         "steps after the timed region: 0 none; 1 HIP events attached to the "
+                         "reorder's kernel dispatches (contiguous KV; the paged cache takes 2); 2 "
+                         "an event pair recorded around every reorder call")
     ap.add_argument("--copy-reference", type=int, default=1,
                     help="time a plain 1 GiB device copy after the timed region")
     return ap.parse_args(argv)
@@ -155,10 +158,18 @@ def bench_search(args, torch, bs, dev):
     hist_dn = torch.empty((n_hist, B), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    # events are created before the timed region; per step, one pair brackets
-    # the KV-reorder launch on the library's stream
+    # events are created before the timed region, one pair per step of the
+    # second pass: either attached to the reorder's kernel dispatch (mode 1,
+    # bs_reorder_kv_timed), so that they take the kernel's own start and end,
+    # or recorded around the reorder call (mode 2)
+    ev_mode = 2 if (paged and args.events == 1) else args.events
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps if args.events else 0)]
+              for _ in range(args.steps if ev_mode else 0)]
+    for e0, e1 in events:  # the handles exist once recorded
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ev_ptrs = [(e0.cuda_event, e1.cuda_event) for e0, e1 in events]
     hist = [(hist_bi[i], hist_tk[i], hist_sc[i], hist_dn[i]) for i in range(n_hist)]
 
     # the timed loop calls the C entry points directly, with every pointer
@@ -173,6 +184,7 @@ def bench_search(args, torch, bs, dev):
     hist_ptrs = [tuple(x.data_ptr() for x in o) for o in hist]
     desc_ref = ctypes.byref(desc)
     step_c, kv_c = L.bs_step, (L.bs_kv_paged_reorder if paged else L.bs_reorder_kv)
+    kv_timed = L.bs_reorder_kv_timed
     kv_h = ph if paged else h
     taken = [0]  # steps of the current search (the library's own count)
 
@@ -182,7 +194,7 @@ def bench_search(args, torch, bs, dev):
             pk.reset()
         taken[0] = 0
 
-    def run(n, record, with_events=False):
+    def run(n, record, with_events=0):
         ts = []
         for i in range(n):
             t = taken[0] % T + 1
@@ -192,12 +204,15 @@ def bench_search(args, torch, bs, dev):
             rc = step_c(h, pool_ptrs[(t - 1) % pool_n], row_stride, *o)
             if rc:
                 raise bs.BeamStepError(rc, "bs_step")
-            if with_events:
+            if with_events == 2:
                 events[i][0].record(stream)
-            rc = kv_c(kv_h, desc_ref, t)
+            if with_events == 1:
+                rc = kv_timed(kv_h, desc_ref, t, *ev_ptrs[i])
+            else:
+                rc = kv_c(kv_h, desc_ref, t)
             if rc:
                 raise bs.BeamStepError(rc, "reorder")
-            if with_events:
+            if with_events == 2:
                 events[i][1].record(stream)
             taken[0] = t
             ts.append(t)
@@ -262,15 +277,15 @@ def bench_search(args, torch, bs, dev):
             prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
         return np.array(kv_bytes, np.float64), np.array(logit_bytes, np.float64)
 
-    # warmup (untimed); the timed region, which records no events, since each
-    # event record stalls the GPU for several microseconds between kernels;
-    # then, for the per-launch durations, the same K steps with a pair of
-    # events around every reorder launch
+    # warmup (untimed); the timed region, which uses no events: an event
+    # record stalls the GPU for several microseconds between kernels, and
+    # events attached to a dispatch slow every step by more; then, for the
+    # per-launch durations, the same K steps with a pair of events per reorder
     reset()
     run(args.warmup, False)
-    ts, elapsed, (kv_bytes, logit_bytes, live_item_steps) = timed(False)
-    if args.events:
-        _, elapsed_ev, (kv_bytes_ev, logit_bytes_ev, _) = timed(True)
+    ts, elapsed, (kv_bytes, logit_bytes, live_item_steps) = timed(0)
+    if ev_mode:
+        _, elapsed_ev, (kv_bytes_ev, logit_bytes_ev, _) = timed(ev_mode)
 
     out = {
         "metric": METRIC,
@@ -301,7 +316,7 @@ def bench_search(args, torch, bs, dev):
         **({} if paged else {"kv_read_write_bytes": list(kv_rw)}),
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
-    if args.events:
+    if ev_mode:
         d_kv = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
         # between one step's reorder and the next: bs_step's two kernels
         d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
@@ -335,11 +350,15 @@ def bench_search(args, torch, bs, dev):
                 "alg_bytes_per_launch": kv_bytes_ev.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
             }
         out["step_kernels"] = {
-            "kernels": "k1_expand_select + k2 (event gap between reorders)",
+            # in the events pass, so it includes what the events cost between
+            # the kernels; the kernel trace gives k1 and k2 themselves
+            "kernels": "k1_expand_select + k2 (gap between reorders, events pass)",
             "avg_us": 1e6 * d_step.mean(),
             "alg_gbs": step_gbs,
         }
-        # the events pass: the same steps, slower by the event records' stalls
+        out["launch_timing"] = ("events attached to the reorder's dispatches" if ev_mode == 1
+                                else "event records around each reorder call")
+        # the events pass: the same steps, slower by the events' stalls
         out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, bpp, planes_n, args.prune)

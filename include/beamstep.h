@@ -195,6 +195,17 @@ typedef struct {
  * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
 int bs_reorder_kv(bs_state *h, const bs_kv_desc *kv, int32_t gen_len);
 
+/* bs_reorder_kv, timed: for callers that measure the reorder's own duration
+ * (benchmarks) without adding records to the stream. start_event and
+ * stop_event are hipEvent_t handles created by the caller (either may be
+ * NULL; the caller keeps ownership). They are attached to the call's first
+ * and last kernel dispatch (hipExtLaunchKernel), so they take the time at
+ * which the reorder kernels start and end, as a kernel trace does. A call
+ * that launches nothing (gen_len 0) records both on the stream back to back.
+ * Errors: as bs_reorder_kv; BS_EDEVICE also if an event cannot be used. */
+int bs_reorder_kv_timed(bs_state *h, const bs_kv_desc *kv, int32_t gen_len,
+                        void *start_event, void *stop_event);
+
 /* Paged KV cache ("llm_internals" 9.2.2, KV-cache paragraph: with a paged
  * cache the reorder becomes a rewrite of block-table entries, and a block is
  * copied only when a shared block is about to be written, i.e. copy on

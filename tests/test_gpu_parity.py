@@ -541,6 +541,30 @@ def test_kv_reorder_layouts(dev, layout, W):
     """The reorder of positions [P, P + t) of every (layer, K|V) plane, for
     the layouts a caller's cache may have, against the oracle's gather; the
     padding between positions and the prompt positions are never written."""
+    _kv_layout_case(dev, layout, W, timed=False)
+
+
+@pytest.mark.parametrize("layout", ["w16_130_planes", "w4_padded_prompt"])
+def test_kv_reorder_timed(dev, layout):
+    """bs_reorder_kv_timed moves the same bytes as bs_reorder_kv, and its
+    events (attached to the first and last dispatch: two launches for 130
+    planes) give a positive duration; with gen_len 0 it launches nothing and
+    still completes both events."""
+    import beam_search_step_amd as bs
+    _kv_layout_case(dev, layout, 16, timed=True)
+    g = bs.BeamSearch(1, 2, 10, 3)
+    g.step(torch.zeros((2, 10), device=dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    plane = torch.zeros((2, 3, 4), dtype=torch.int32, device=dev)
+    bs.bs_reorder_kv_timed(g.h, bs.make_kv_desc([plane]), 0, e0.cuda_event, e1.cuda_event)
+    e1.synchronize()
+    assert e0.elapsed_time(e1) >= 0
+    g.close()
+
+
+def _kv_layout_case(dev, layout, W, timed):
     import beam_search_step_amd as bs
     words, pad, P, n_planes = KV_LAYOUTS[layout]
     B, V, T = 3, 40, 7
@@ -566,7 +590,15 @@ def test_kv_reorder_layouts(dev, layout, W):
                 .astype(np.int32)
             f[:, P + t - 1, :words] = torch.from_numpy(vals).to(dev)
             h[:, P + t - 1] = vals
-        g.reorder_kv(desc, t)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()   # the handles exist once recorded
+            e1.record()
+            bs.bs_reorder_kv_timed(g.h, desc, t, e0.cuda_event, e1.cuda_event)
+            e1.synchronize()
+            assert e0.elapsed_time(e1) > 0, f"{layout} W={W} t={t}: no duration"
+        else:
+            g.reorder_kv(desc, t)
         oracle.kv_reorder(host, obi, odn, t, pos_offset=P)
         for li, (f, h, f0) in enumerate(zip(full, host, full0)):
             got = f.cpu().numpy()
