@@ -85,10 +85,13 @@ struct bs_state {
   int* qj;
   int* qn;
   bs_kv_paged* paged;   // the paged cache whose table update bs_step runs
+  bs_kv_paged* caches;  // every paged cache created on the handle (linked)
 };
 
 struct bs_kv_paged {
-  bs_state* h;
+  bs_state* h;          // null once the handle is destroyed (the cache is orphaned)
+  bs_kv_paged* next;    // the handle's next cache
+  hipStream_t stream;   // the handle's stream
   int bs, bpi, mb;
   int last_t;   // the step last reordered (0: none since the reset)
   int table_t;  // the step whose table update has run (0: none since the reset)
@@ -668,6 +671,7 @@ int bs_kv_paged_create(bs_state* h, int32_t block_size, int32_t blocks_per_item,
   bs_kv_paged* p = (bs_kv_paged*)calloc(1, sizeof(bs_kv_paged));
   if (!p) return BS_ENOMEM;
   p->h = h;
+  p->stream = h->stream;
   p->bs = block_size;
   p->bpi = blocks_per_item;
   p->mb = mb;
@@ -710,12 +714,15 @@ int bs_kv_paged_create(bs_state* h, int32_t block_size, int32_t blocks_per_item,
     return rc;
   }
   if (!h->paged) h->paged = p;  // the first cache of a handle: bs_step runs its table update
+  p->next = h->caches;
+  h->caches = p;
   *out = p;
   return BS_OK;
 }
 
 int bs_kv_paged_reset(bs_kv_paged* p) {
   if (!p) return BS_EINVAL;
+  if (!p->h) return BS_ESTATE;
   hipLaunchKernelGGL(k6_paged_init, dim3(p->h->B), dim3(kThreads), 0, p->h->stream, p->pg,
                      p->h->B, p->h->W, p->bpi, p->mb);
   const int rc = launch_status();
@@ -725,6 +732,7 @@ int bs_kv_paged_reset(bs_kv_paged* p) {
 
 int bs_kv_paged_table(const bs_kv_paged* p, int32_t** table, int32_t* max_blocks) {
   if (!p || !table || !max_blocks) return BS_EINVAL;
+  if (!p->h) return BS_ESTATE;
   *table = p->pg.table;
   *max_blocks = p->mb;
   return BS_OK;
@@ -738,6 +746,7 @@ int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len)
       (int64_t)(p->bs - 1) * pool->pos_stride + pool->bytes_per_pos > pool->block_stride)
     return BS_EINVAL;
   bs_state* h = p->h;
+  if (!h) return BS_ESTATE;
   // every step is reordered once, in order: the table of step t is built on
   // that of step t-1
   if (h->t == 0 || gen_len != h->t || p->last_t + 1 != h->t) return BS_ESTATE;
@@ -792,6 +801,7 @@ int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len)
 
 int bs_kv_paged_status(bs_kv_paged* p, int32_t* overflow, int32_t* free_blocks) {
   if (!p || !overflow) return BS_EINVAL;
+  if (!p->h) return BS_ESTATE;
   hipStream_t s = p->h->stream;
   if (hipStreamSynchronize(s) != hipSuccess) return BS_EDEVICE;
   if (hipMemcpy(overflow, p->pg.overflow, 4, hipMemcpyDeviceToHost) != hipSuccess)
@@ -805,8 +815,15 @@ int bs_kv_paged_status(bs_kv_paged* p, int32_t* overflow, int32_t* free_blocks) 
 
 void bs_kv_paged_destroy(bs_kv_paged* p) {
   if (!p) return;
-  if (p->h->paged == p) p->h->paged = nullptr;
-  (void)hipStreamSynchronize(p->h->stream);
+  if (p->h) {  // unlink from the handle
+    if (p->h->paged == p) p->h->paged = nullptr;
+    for (bs_kv_paged** q = &p->h->caches; *q; q = &(*q)->next)
+      if (*q == p) {
+        *q = p->next;
+        break;
+      }
+  }
+  (void)hipStreamSynchronize(p->stream);
   (void)hipFree(p->block);
   free(p);
 }
@@ -860,6 +877,7 @@ int bs_steps_taken(const bs_state* h) { return h ? h->t : BS_EINVAL; }
 
 void bs_destroy(bs_state* h) {
   if (!h) return;
+  for (bs_kv_paged* p = h->caches; p; p = p->next) p->h = nullptr;  // orphaned
   (void)hipStreamSynchronize(h->stream);
   (void)hipFree(h->block);
   free(h);

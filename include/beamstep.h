@@ -240,8 +240,9 @@ typedef struct {
  * the fused selection and a row spans at most 64 tiles of its streaming pass
  * (V <= 64 * 256 * the logits per thread, tile_elems or the library's
  * choice), and bs_kv_paged_reorder then only makes the copies. The table
- * therefore shows step t's blocks from that bs_step on. Destroy a cache
- * before its handle.
+ * therefore shows step t's blocks from that bs_step on. A cache whose
+ * handle is destroyed first is orphaned: every later call on it returns
+ * BS_ESTATE, except bs_kv_paged_destroy, which frees it.
  *   block_size       positions per block, >= 1
  *   blocks_per_item  W <= blocks_per_item <= 4096; W * max_blocks always
  *                    suffices, fewer relies on shared prefixes

@@ -235,4 +235,13 @@ def test_paged_error_paths(dev):
         pk.reorder(pools, 3)                   # step 2 was never reordered
     torch.cuda.synchronize()
     pk.close()
+    # a cache whose handle is destroyed first is orphaned, and still freed cleanly
+    pk2 = bs.PagedKV(g, 4)
     g.close()
+    with pytest.raises(bs.BeamStepError) as e:
+        pk2.reset()
+    assert e.value.status == bs.BS_ESTATE
+    with pytest.raises(bs.BeamStepError) as e:
+        pk2.reorder(pools, 1)
+    assert e.value.status == bs.BS_ESTATE
+    pk2.close()
