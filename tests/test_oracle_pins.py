@@ -556,3 +556,25 @@ def test_verify_workload_acceptance_rate(orc):
     freq = np.bincount(acc, minlength=k + 1)[1:] / acc.size
     want = [p ** (m - 1) * (1 - p) for m in range(1, k)] + [p ** (k - 1)]
     assert np.abs(freq - np.array(want)).max() < 0.04, (freq, want)
+
+
+def test_workload_sizes_match_the_pages_arithmetic():
+    """The Llama-3-8B-shaped workload against the figures "llm_internals"
+    prints for it: 4 beams over a 128,256-token vocabulary give 513,024
+    candidates per item (9.2.2, step 3); one token's KV is 65,536 values,
+    128 KiB in bf16 (9.2.4); with the 1,000-token prompt stored once, 4 beams
+    after 200 generated tokens hold 1,800 tokens (225 MiB) instead of 4,800
+    (600 MiB). The other workloads' KV per token as their shapes state it."""
+    wl = synth.WORKLOADS["llama3_8b"]
+    assert wl.beam * wl.vocab == 513_024
+    assert wl.kv_bytes_per_token // wl.kv_elem_bytes == 65_536
+    assert wl.kv_bytes_per_token == 128 * 1024
+    shared = wl.prompt_len + wl.beam * wl.max_steps
+    naive = wl.beam * (wl.prompt_len + wl.max_steps)
+    assert (shared, naive) == (1_800, 4_800)
+    assert shared * wl.kv_bytes_per_token == 225 * 2 ** 20
+    assert naive * wl.kv_bytes_per_token == 600 * 2 ** 20
+    assert synth.WORKLOADS["tbase"].kv_bytes_per_token == 6 * 2 * 8 * 64 * 4   # 24 KiB
+    assert synth.WORKLOADS["wide"].kv_bytes_per_token == 6 * 2 * 16 * 64 * 4   # 48 KiB
+    assert synth.WORKLOADS["toy"].kv_bytes_per_token == 64
+    assert synth.WORKLOADS["wide"].beam * synth.WORKLOADS["wide"].vocab == 4_000_000
