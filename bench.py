@@ -239,43 +239,10 @@ def bench_search(args, torch, bs, dev):
     kv_rw = [0, 0]  # KV bytes read (distinct parents) and written (moved slots)
 
     def step_bytes(ts, bi, sc, dn):
-        kv_rw[0] = kv_rw[1] = 0
-        kv_bytes = []
-        logit_bytes = []
-        prev_live = np.zeros((B, W), bool)
-        for i, t in enumerate(ts):
-            if t == 1:
-                prev_live = np.zeros((B, W), bool)
-                prev_live[:, 0] = True
-            live_rows = int(prev_live.sum())                  # rows the step had to read
-            logit_bytes.append(live_rows * V * wl.elem_bytes + 20 * B * W)
-            if paged:
-                # copies on write: live slots beyond the first of each parent,
-                # t % block_size positions each, read and written in every pool;
-                # plus the items' tables, reference counts and free lists
-                copies = 0
-                if t % bsz:
-                    for b in range(B):
-                        if dn[i, b]:
-                            continue
-                        lv = [w for w in range(W) if sc[i, b, w] > -np.inf]
-                        copies += len(lv) - len({int(bi[i, b, w]) for w in lv})
-                kv_bytes.append(2 * copies * (t % bsz) * bpp * planes_n
-                                + 2 * B * (W * pk.max_blocks + 2 * pk.blocks_per_item) * 4)
-            else:
-                moved_total = 0
-                for b in range(B):
-                    if dn[i, b]:
-                        continue
-                    live = sc[i, b] > -np.inf
-                    moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
-                    parents = {int(bi[i, b, w]) for w in moved}
-                    moved_total += len(moved) + len(parents)
-                    kv_rw[0] += len(parents) * t * bpp * planes_n
-                    kv_rw[1] += len(moved) * t * bpp * planes_n
-                kv_bytes.append(moved_total * t * bpp * planes_n)
-            prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
-        return np.array(kv_bytes, np.float64), np.array(logit_bytes, np.float64)
+        kv, lb, kv_rw[0], kv_rw[1] = algorithmic_bytes(
+            ts, bi, sc, dn, V, wl.elem_bytes, bpp, planes_n,
+            paged=(bsz, pk.max_blocks, pk.blocks_per_item) if paged else None)
+        return kv, lb
 
     # warmup (untimed); the timed region, which uses no events: an event
     # record stalls the GPU for several microseconds between kernels, and
@@ -323,6 +290,16 @@ def bench_search(args, torch, bs, dev):
                            for i in range(1, len(events))]) * 1e-3
         ach = kv_bytes_ev.sum() / d_kv.sum() / 1e9
         step_gbs = logit_bytes_ev[1:].sum() / d_step.sum() / 1e9
+        # the reorder over a search: mean duration and rate of its launches at
+        # a few steps t (every search of the pass that reached that step)
+        tsa = np.array(ts)
+        curve = {}
+        for tq in sorted({1, T // 4, T // 2, 3 * T // 4, T}):
+            sel = tsa == tq
+            if sel.any() and d_kv[sel].sum() > 0:
+                curve[str(tq)] = {"us": 1e6 * d_kv[sel].mean(),
+                                  "GBs": kv_bytes_ev[sel].sum() / d_kv[sel].sum() / 1e9}
+        out["reorder_by_step"] = curve
         if paged:
             # the logits pass dominates once the reorder moves only partial blocks;
             # with the cache attached to the handle, bs_step's k2 also runs the
@@ -478,6 +455,58 @@ def bench_verify(args, torch, bs, dev):
     out["input_generation_s"] = gen_s
     ver.close()
     return out
+
+
+def algorithmic_bytes(ts, bi, sc, dn, V, elem_bytes, bpp, planes, paged=None):
+    """The HBM bytes each step of a run must move, from its recorded outputs.
+
+    ts: the step t of every run step (t = 1 starts a search); bi, sc, dn: the
+    step's beam_idx [B, W], scores [B, W] and done [B] as bs_step returned
+    them. A step reads the logits of the rows live before it (slot 0 of each
+    item at t = 1), plus 20 bytes of state and outputs per row. The contiguous
+    reorder reads each distinct parent of the moved slots once and writes each
+    moved slot (a live slot whose parent is another slot), t positions of
+    bpp bytes in every plane, for items not done after the step. The paged
+    reorder (paged = (block_size, max_blocks, blocks_per_item)) reads and
+    writes t % block_size positions for every live slot beyond the first child
+    of its parent, plus the items' tables, reference counts and free lists.
+    Returns (KV bytes per step, logit bytes per step, KV bytes read, KV bytes
+    written), the last two for the contiguous reorder only."""
+    n, B, W = bi.shape
+    kv_bytes, logit_bytes = [], []
+    kv_read = kv_written = 0
+    prev_live = np.zeros((B, W), bool)
+    for i, t in enumerate(ts):
+        if t == 1:
+            prev_live = np.zeros((B, W), bool)
+            prev_live[:, 0] = True
+        logit_bytes.append(int(prev_live.sum()) * V * elem_bytes + 20 * B * W)
+        if paged:
+            bsz, max_blocks, bpi = paged
+            copies = 0
+            if t % bsz:
+                for b in range(B):
+                    if dn[i, b]:
+                        continue
+                    lv = [w for w in range(W) if sc[i, b, w] > -np.inf]
+                    copies += len(lv) - len({int(bi[i, b, w]) for w in lv})
+            kv_bytes.append(2 * copies * (t % bsz) * bpp * planes
+                            + 2 * B * (W * max_blocks + 2 * bpi) * 4)
+        else:
+            moved_total = 0
+            for b in range(B):
+                if dn[i, b]:
+                    continue
+                live = sc[i, b] > -np.inf
+                moved = [w for w in range(W) if live[w] and bi[i, b, w] != w]
+                parents = {int(bi[i, b, w]) for w in moved}
+                moved_total += len(moved) + len(parents)
+                kv_read += len(parents) * t * bpp * planes
+                kv_written += len(moved) * t * bpp * planes
+            kv_bytes.append(moved_total * t * bpp * planes)
+        prev_live = (sc[i] > -np.inf) & ~dn[i][:, None]
+    return (np.array(kv_bytes, np.float64), np.array(logit_bytes, np.float64),
+            kv_read, kv_written)
 
 
 def copy_reference(torch, dev):

@@ -77,3 +77,45 @@ def test_traffic_summaries_are_consistent():
         # a summary taken on an earlier version of the kernel is not reported
         current = d["source_sha256_16"] == bench.kernel_source_hash(kernel)
         assert found == (got if current else None), p
+
+
+def test_algorithmic_bytes_by_hand():
+    """The byte accounting behind every GB/s figure, on hand-worked steps:
+    B=2 items, W=3 beams, V=10 fp32 logits, 16-byte positions, 2 planes."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import bench
+    inf = -np.inf
+    f = 0.0
+    ts = [1, 2, 3, 1]
+    bi = np.array([[[0, 0, 0], [0, 0, 0]],      # t=1: one parent for every slot
+                   [[1, 0, 2], [0, 0, 0]],      # t=2: item 0 swaps slots 0 and 1
+                   [[2, 2, 2], [0, 1, 2]],      # t=3: item 0 copies slot 2 twice
+                   [[0, 0, 0], [0, 0, 0]]])     # t=1 again: a new search
+    sc = np.array([[[f, f, f], [f, f, inf]],    # item 1 has a dead slot
+                   [[f, f, f], [f, f, f]],
+                   [[f, f, f], [inf, inf, inf]],
+                   [[f, f, f], [f, f, f]]])
+    dn = np.array([[0, 0], [0, 1], [0, 1], [0, 0]], bool)   # item 1 done after t=2
+    kv, lg, rd, wr = bench.algorithmic_bytes(ts, bi, sc, dn, V=10, elem_bytes=4, bpp=16,
+                                             planes=2)
+    per = 16 * 2  # one position of one row in every plane
+    # t=1: item 0 moves slots 1, 2 from parent 0 (2 writes + 1 read); item 1
+    # moves slot 1 (its slot 2 is dead): 1 write + 1 read
+    # t=2: item 0 swaps: 2 writes + 2 reads; item 1 is done: nothing
+    # t=3: item 0 writes slots 0, 1 from parent 2: 2 writes + 1 read
+    # t=1 (new search): both items move slots 1, 2 from parent 0
+    assert kv.tolist() == [5 * 1 * per, 4 * 2 * per, 3 * 3 * per, 6 * 1 * per]
+    # logits of the rows live before the step: 2 (slot 0 of each item), then
+    # 3 + 2, then 3 (item 1 done), then 2 again; plus 20 bytes per row
+    state = 20 * 2 * 3
+    assert lg.tolist() == [2 * 40 + state, 5 * 40 + state, 3 * 40 + state, 2 * 40 + state]
+    assert rd == (2 * 1 + 2 * 2 + 1 * 3 + 2 * 1) * per
+    assert wr == (3 * 1 + 2 * 2 + 2 * 3 + 4 * 1) * per
+    # paged, blocks of 2 positions: copies only where t is inside a block
+    # (t = 1 and 3): live slots beyond the first child of each parent
+    kvp, _, _, _ = bench.algorithmic_bytes(ts, bi, sc, dn, V=10, elem_bytes=4, bpp=16,
+                                           planes=2, paged=(2, 5, 12))
+    tables = 2 * 2 * (3 * 5 + 2 * 12) * 4
+    copies = [2 + 1, 0, 2, 2 + 2]
+    assert kvp.tolist() == [2 * c * (t % 2) * per + tables for c, t in zip(copies, ts)]
