@@ -25,6 +25,8 @@ BS_PRUNE_TOPW, BS_PRUNE_TOP2W = 0, 1
 BS_SELECT_FUSED, BS_SELECT_TWO_PASS = 0, 1
 
 DTYPES = {"f32": BS_F32, "bf16": BS_BF16}
+# torch dtypes that hold each logits type (bf16 may come as its 16-bit pattern)
+LOGIT_DTYPES = {"f32": {"float32"}, "bf16": {"bfloat16", "int16", "uint16"}}
 LPS = {"none": BS_LP_NONE, "gnmt": BS_LP_GNMT, "pow": BS_LP_POW}
 STOPS = {"true": BS_STOP_TRUE, "heuristic": BS_STOP_HEURISTIC, "never": BS_STOP_NEVER}
 PRUNES = {"topw": BS_PRUNE_TOPW, "top2w": BS_PRUNE_TOP2W}
@@ -127,6 +129,55 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _rows(t, what: str, rows: int = 0, cols: int = 0, dtypes=None, need_gpu: bool = True) -> int:
+    """Row stride, in elements, of a tensor of rows [rows, n] or [a, b, n]
+    (row r at r * stride), after checking that it can hold what a kernel
+    will read or write: at least ``rows`` rows of ``cols`` contiguous
+    elements, evenly spaced, of one of ``dtypes``, on the GPU. The library
+    takes plain pointers and cannot check sizes itself."""
+    if need_gpu and not t.is_cuda:
+        raise ValueError(f"{what}: a GPU tensor is needed")
+    if dtypes and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of {sorted(dtypes)}")
+    if t.dim() not in (2, 3) or t.stride(-1) != 1:
+        raise ValueError(f"{what}: rows of contiguous elements expected, [rows, n] or [a, b, n]")
+    if t.dim() == 3 and t.shape[0] > 1 and t.shape[1] > 1 and t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError(f"{what}: rows of [a, b, n] must be evenly spaced")
+    n = t.shape[0] if t.dim() == 2 else t.shape[0] * t.shape[1]
+    if n < rows:
+        raise ValueError(f"{what}: {n} rows, {rows} needed")
+    if t.shape[-1] < cols:
+        raise ValueError(f"{what}: rows of {t.shape[-1]} elements, {cols} needed")
+    if t.dim() == 2 or t.shape[1] > 1:
+        stride = t.stride(-2)
+    else:
+        stride = t.stride(0)
+    return max(stride, t.shape[-1]) if n == 1 else stride
+
+
+def _check_planes(planes, what: str, rows: int, positions: int) -> None:
+    """KV planes (or block pools) as tensors [rows, positions, ...]: all of one
+    shape, strides and dtype, on the GPU, holding ``rows`` rows of
+    ``positions`` positions."""
+    p0 = planes[0]
+    for i, p in enumerate(planes):
+        if not p.is_cuda:
+            raise ValueError(f"{what} {i}: a GPU tensor is needed")
+        if p.shape != p0.shape or p.stride() != p0.stride() or p.dtype != p0.dtype:
+            raise ValueError(f"{what} {i}: every plane must have the shape, strides and dtype "
+                             f"of the first")
+    if p0.dim() < 2 or p0.shape[0] < rows or p0.shape[1] < positions:
+        raise ValueError(f"{what}: shape {tuple(p0.shape)}, at least [{rows}, {positions}, ...] "
+                         f"needed")
+    if p0[0, 0].numel() != 1 and not p0[0, 0].is_contiguous():
+        raise ValueError(f"{what}: the elements of a position must be contiguous")
+
+
+def _torch_int32():
+    import torch
+    return torch.int32
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -153,9 +204,8 @@ def bs_reset(h: int) -> None:
 
 
 def bs_step(h: int, logits, beam_idx, token_id, scores, done) -> None:
-    stride = logits.stride(0) if logits.dim() == 2 else logits.shape[-1]
-    _check(library().bs_step(h, _ptr(logits), stride, _ptr(beam_idx), _ptr(token_id),
-                             _ptr(scores), _ptr(done)), "bs_step")
+    _check(library().bs_step(h, _ptr(logits), _rows(logits, "logits"), _ptr(beam_idx),
+                             _ptr(token_id), _ptr(scores), _ptr(done)), "bs_step")
 
 
 def make_kv_desc(planes: Sequence, pos_offset: int = 0) -> bs_kv_desc:
@@ -259,13 +309,7 @@ def bs_verify_create(batch: int, k: int, vocab: int, dtype: int, stream=None) ->
 
 def _verify_stride(logits) -> int:
     """Row stride in elements of logits [B*k, S] or [B, k, S] (rows evenly spaced)."""
-    if logits.stride(-1) != 1:
-        raise ValueError("logits rows must be contiguous")
-    if logits.dim() == 3:
-        if logits.shape[0] > 1 and logits.stride(0) != logits.shape[1] * logits.stride(1):
-            raise ValueError("rows of logits [B, k, S] must be evenly spaced")
-        return logits.stride(1)
-    return logits.stride(0)
+    return _rows(logits, "logits")
 
 
 def bs_verify(h: int, logits, proposals, accept_len, argmax) -> None:
@@ -302,6 +346,7 @@ class BeamSearch:
                  prune="topw", select="fused", stream=None):
         import torch
         self.B, self.W, self.V, self.T = batch, beam, vocab, max_steps
+        self.dtype = dtype
         self.K = 2 * beam if prune == "top2w" else beam   # candidates ranked per item
         self.num_return = num_return
         self.cfg = bs_config(batch, beam, vocab, max_steps, eos_id, pad_id, DTYPES[dtype],
@@ -343,12 +388,14 @@ class BeamSearch:
         return bs_steps_taken(self.h)
 
     def step(self, logits):
+        _rows(logits, "logits", self.B * self.W, self.V, LOGIT_DTYPES[self.dtype])
         bs_step(self.h, logits, self.beam_idx, self.token_id, self.scores, self.done)
         return self.beam_idx, self.token_id, self.scores, self.done
 
     def reorder_kv(self, planes_or_desc, gen_len: int, pos_offset: int = 0):
         d = planes_or_desc
         if not isinstance(d, bs_kv_desc):
+            _check_planes(d, "KV plane", self.B * self.W, pos_offset + gen_len)
             d = make_kv_desc(d, pos_offset)
         bs_reorder_kv(self.h, d, gen_len)
 
@@ -411,6 +458,7 @@ class PagedKV:
     def reorder(self, pools_or_desc, gen_len: int):
         d = pools_or_desc
         if not isinstance(d, bs_kv_pool):
+            _check_planes(d, "block pool", self.search.B * self.blocks_per_item, self.block_size)
             d = make_kv_pool(d)
         bs_kv_paged_reorder(self.h, d, gen_len)
 
@@ -445,6 +493,7 @@ class Verifier:
     def __init__(self, batch, k, vocab, dtype="f32", stream=None):
         import torch
         self.B, self.k, self.V = batch, k, vocab
+        self.dtype = dtype
         self.h = bs_verify_create(batch, k, vocab, DTYPES[dtype], stream)
         dev = torch.device("cuda", torch.cuda.current_device())
         self.accept_len = torch.empty(batch, dtype=torch.int32, device=dev)
@@ -464,6 +513,11 @@ class Verifier:
     def __call__(self, logits, proposals, top_k=1, min_block=0, rank=False):
         """Exact verify by default; top_k > 1 or min_block > 1 gives the
         approximate criteria. With rank=True also returns each proposal's rank."""
+        _rows(logits, "logits", self.B * self.k, self.V, LOGIT_DTYPES[self.dtype])
+        if not proposals.is_cuda or proposals.dtype != _torch_int32() or \
+                not proposals.is_contiguous() or proposals.numel() < self.B * self.k:
+            raise ValueError(f"proposals: a contiguous GPU int32 tensor of {self.B * self.k} "
+                             f"elements is needed")
         if top_k == 1 and min_block == 0 and not rank:
             bs_verify(self.h, logits, proposals, self.accept_len, self.argmax)
             return self.accept_len, self.argmax

@@ -91,3 +91,29 @@ def test_config_struct_layout_matches_header():
     # int32 then a pointer (8-aligned), then three int64
     assert ctypes.sizeof(bs.bs_kv_pool) == 40
     assert bs.bs_kv_pool.block_stride.offset == 16
+
+
+def test_binding_checks_tensor_layouts():
+    """The wrappers check a tensor before its pointer reaches a kernel: the
+    library cannot see sizes, so too few rows or columns, non-contiguous rows,
+    unevenly spaced rows or a wrong dtype would otherwise be read or written
+    out of bounds."""
+    import torch
+    import beam_search_step_amd as bs
+    f32 = {"float32"}
+    ok = torch.zeros(12, 100)
+    assert bs._rows(ok, "x", 12, 100, f32, need_gpu=False) == 100
+    assert bs._rows(ok.view(3, 4, 100), "x", 12, 100, f32, need_gpu=False) == 100
+    assert bs._rows(torch.zeros(12, 128)[:, :100], "x", 12, 100, f32, need_gpu=False) == 128
+    assert bs._rows(torch.zeros(1, 100), "x", 1, 100, f32, need_gpu=False) == 100
+    bad = [torch.zeros(11, 100),                       # too few rows
+           torch.zeros(12, 99),                        # rows too short
+           torch.zeros(100, 12).t(),                   # columns not contiguous
+           torch.zeros(3, 5, 100)[:, :4],              # [a, b, n] rows unevenly spaced
+           torch.zeros(12, 100, dtype=torch.float64),  # wrong dtype
+           torch.zeros(1200)]                          # not rows
+    for t in bad:
+        with pytest.raises(ValueError):
+            bs._rows(t, "x", 12, 100, f32, need_gpu=False)
+    with pytest.raises(ValueError):                    # a CPU tensor
+        bs._rows(ok, "x", 12, 100, f32)

@@ -472,6 +472,42 @@ def test_error_paths_on_device(dev):
     g.close()
 
 
+def test_wrappers_reject_bad_tensors_before_launching(dev):
+    """The Python wrappers refuse tensors a kernel would read or write out of
+    bounds, before any launch; the handle's state is unchanged."""
+    import beam_search_step_amd as bs
+    g = bs.BeamSearch(2, 3, 50, 4)
+    for bad in (torch.zeros((5, 50), device=dev),                    # 5 rows of 6
+                torch.zeros((6, 49), device=dev),                    # rows too short
+                torch.zeros((6, 50), device=dev, dtype=torch.float16),
+                torch.zeros((50, 6), device=dev).t(),                # not contiguous
+                torch.zeros((6, 50))):                               # on the host
+        with pytest.raises(ValueError):
+            g.step(bad)
+    assert g.steps == 0
+    g.step(torch.zeros((6, 50), device=dev))
+    with pytest.raises(ValueError):                                  # 5 rows of 6
+        g.reorder_kv([torch.zeros((5, 4, 4), dtype=torch.int32, device=dev)], 1)
+    with pytest.raises(ValueError):                                  # 1 position of 2
+        g.reorder_kv([torch.zeros((6, 1, 4), dtype=torch.int32, device=dev)], 1, pos_offset=1)
+    with pytest.raises(ValueError):                                  # planes differ
+        g.reorder_kv([torch.zeros((6, 4, 4), dtype=torch.int32, device=dev),
+                      torch.zeros((6, 3, 4), dtype=torch.int32, device=dev)], 1)
+    g.reorder_kv([torch.zeros((6, 4, 4), dtype=torch.int32, device=dev)], 1)
+    g.close()
+    v = bs.Verifier(2, 3, 40)
+    lg = torch.zeros((2, 3, 40), device=dev)
+    with pytest.raises(ValueError):
+        v(torch.zeros((2, 2, 40), device=dev), torch.zeros((2, 3), dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):
+        v(lg, torch.zeros((2, 3), dtype=torch.int64, device=dev))
+    with pytest.raises(ValueError):
+        v(lg, torch.zeros((2, 2), dtype=torch.int32, device=dev))
+    acc, am = v(lg, torch.zeros((2, 3), dtype=torch.int32, device=dev))
+    assert acc.cpu().tolist() == [3, 3]
+    v.close()
+
+
 def test_reset_reproduces_and_is_deterministic(dev):
     import beam_search_step_amd as bs
     wl = synth.WORKLOADS["tbase"].replace(batch=8, max_steps=12)
