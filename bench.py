@@ -83,6 +83,10 @@ def parse(argv=None):
                          "steps after the timed region: 0 none; 1 HIP events attached to the "
                          "reorder's kernel dispatches (contiguous KV; the paged cache takes 2); 2 "
                          "an event pair recorded around every reorder call")
+    ap.add_argument("--graph", type=int, default=0, choices=[0, 1],
+                    help="also time the K steps replayed from one HIP graph captured on the "
+                         "library's stream (no host issue cost per launch); value is then the "
+                         "graph's rate")
     ap.add_argument("--copy-reference", type=int, default=1,
                     help="time a plain 1 GiB device copy after the timed region")
     return ap.parse_args(argv)
@@ -138,8 +142,11 @@ def bench_search(args, torch, bs, dev):
         for i in range(s, pool_n, distinct_n):
             pool[i].copy_(src)
     gen_s = time.time() - t0
+    # the library's stream: a stream of its own when the steps are captured
+    # into a graph (the legacy default stream cannot be captured)
+    lib_stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
     g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems,
-                                   select=args.select)
+                                   select=args.select, stream=lib_stream)
     paged = args.kv == "paged"
     bsz = args.block_size
     if paged:
@@ -156,7 +163,7 @@ def bench_search(args, torch, bs, dev):
     hist_tk = torch.empty_like(hist_bi)
     hist_sc = torch.empty((n_hist, B, W), dtype=torch.float32, device=dev)
     hist_dn = torch.empty((n_hist, B), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    stream = lib_stream
 
     # events are created before the timed region, one pair per step of the
     # second pass: either attached to the reorder's kernel dispatch (mode 1,
@@ -228,6 +235,22 @@ def bench_search(args, torch, bs, dev):
         torch.cuda.synchronize()
         return ts, time.perf_counter() - t_start, alg_bytes(ts)
 
+    def timed_graph():
+        """The same K steps, from a fresh search, captured once into a HIP
+        graph on the library's stream and replayed: the GPU runs the same
+        launches with the same arguments, without the host's issue cost."""
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=lib_stream):
+            reset()
+            ts = run(args.steps, True, 0)
+        graph.replay()  # untimed
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        return ts, time.perf_counter() - t_start, alg_bytes(ts)
+
     # ---- algorithmic bytes from the recorded step outputs -----------------------
     def alg_bytes(ts):
         bi = hist_bi.cpu().numpy()
@@ -251,6 +274,10 @@ def bench_search(args, torch, bs, dev):
     reset()
     run(args.warmup, False)
     ts, elapsed, (kv_bytes, logit_bytes, live_item_steps) = timed(0)
+    eager_elapsed = elapsed
+    if args.graph:
+        ts_g, elapsed, (kv_bytes_g, _, _) = timed_graph()
+        assert ts_g == ts and np.array_equal(kv_bytes_g, kv_bytes), "graph replay differs"
     if ev_mode:
         _, elapsed_ev, (kv_bytes_ev, logit_bytes_ev, _) = timed(ev_mode)
 
@@ -279,6 +306,9 @@ def bench_search(args, torch, bs, dev):
             **({"block_size": bsz} if paged else {}),
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
+        "launch": "one HIP graph of the timed steps, replayed" if args.graph
+                  else "the C entry points called from the host, step by step",
+        **({"eager_value": args.steps / eager_elapsed} if args.graph else {}),
         "live_item_steps": live_item_steps,
         **({} if paged else {"kv_read_write_bytes": list(kv_rw)}),
     }

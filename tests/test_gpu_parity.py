@@ -675,3 +675,57 @@ def test_kv_reorder_patterns(dev, name):
     else:
         assert osc[0, 3] == -np.inf and obi[0, 3] == 3   # dead slot keeps its row
     g.close()
+
+
+def test_graph_capture_replays_match_eager(dev):
+    """A search captured into one HIP graph (bs_reset, six bs_step and
+    bs_reorder_kv calls, on the handle's own stream) and replayed three times,
+    with eager work and synchronisation between the replays: every replay's
+    per-step outputs and final KV planes equal the eager run's. The calls
+    allocate nothing and record no memset, so they can be captured."""
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["toy"].replace(batch=3, beam=4, vocab=40, max_steps=6, eos_id=3,
+                                        eos_in_zipf=False, seed=91)
+    T, rows = wl.max_steps, wl.rows
+    stream = torch.cuda.Stream()
+    g = bs.BeamSearch.for_workload(wl, stream=stream)
+    lgs = [torch.from_numpy(synth.logits(wl, t)).to(dev) for t in range(1, T + 1)]
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    pristine = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, T, 8), generator=gen,
+                             dtype=torch.int32).to(dev)
+    plane = torch.empty_like(pristine)
+    outs = lambda: [torch.empty((T, wl.batch, wl.beam), dtype=dt, device=dev)
+                    for dt in (torch.int32, torch.int32, torch.float32)]
+
+    def search(hist):
+        torch.add(pristine, 0, out=plane)
+        g.reset()
+        for t in range(1, T + 1):
+            bi, tk, sc, dn = g.step(lgs[t - 1])
+            for h, x in zip(hist, (bi, tk, sc)):
+                torch.add(x, 0, out=h[t - 1])
+            g.reorder_kv([plane], t)
+
+    eager = outs()
+    with torch.cuda.stream(stream):
+        search(eager)
+    torch.cuda.synchronize()
+    eager_plane = plane.clone()
+    replayed = outs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        search(replayed)
+    for rep in range(3):
+        noise = torch.randn(1000, device=dev).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        for h in replayed:
+            h.zero_()
+        plane.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(replayed, eager):
+            assert torch.equal(a, b), f"replay {rep}: outputs differ"
+        assert torch.equal(plane, eager_plane), f"replay {rep}: KV differs"
+        assert noise.isfinite()
+    g.close()
