@@ -658,6 +658,8 @@ __device__ __forceinline__ float row16_sum_f(float v) {
 // Stage B, wave 0: the W row lists are merged the same way (lane w holds row
 // w's list; a lower row means a lower flat index), and the K winners are put
 // in exact (score desc, flat index asc) order before the finalize.
+// The workgroup has 256 threads, or 64 when W <= 4 (one wave holds the row
+// groups of 4 rows; every use of the thread index stays below 64 then).
 template <int WMAX, int H>
 __device__ __forceinline__ void select_finalize_item(const K2Args& a) {
   __shared__ HypSmem<WMAX> hy;
