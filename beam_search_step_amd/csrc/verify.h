@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k4_row(K4Args a) {
       for (int q0 = qs + tid; q0 < qe; q0 += kThreads * kRowLoads) {
         uint4 raw[kRowLoads];
 #pragma unroll
-        for (int u = 0; u < kRowLoads; ++u) raw[u] = rv[min(q0 + u * kThreads, qmax)];
+        for (int u = 0; u < kRowLoads; ++u) raw[u] = load16_stream(&rv[min(q0 + u * kThreads, qmax)]);
 #pragma unroll
         for (int u = 0; u < kRowLoads; ++u) {
           const int q = q0 + u * kThreads;
