@@ -19,6 +19,8 @@ struct K3Args {
   int W;
   const int* plan;
   int whole_planes;     // 1: XCD i takes the i-th eighth of the planes
+  int stream_loads;     // 1: parent words are read with the nontemporal hint
+  int64_t region_bytes_per_plane;  // rows x gen_len x bytes_per_pos (host side)
 };
 
 template <int WORD>
@@ -40,18 +42,30 @@ template <int WMAX, typename WT, int NP, bool FULL>
 __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row_stride,
                                            const int64_t (&off)[NP], int64_t e0, int64_t words,
                                            int nsrc, const int (&src)[WMAX],
-                                           const int (&dmask)[WMAX]) {
+                                           const int (&dmask)[WMAX], bool stream_loads) {
   bool ok[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) ok[k] = FULL || e0 + (int64_t)k * kK3Threads < words;
   WT v[NP][WMAX];
+  if (stream_loads) {  // uniform: one loop each way, so no load waits on a branch
 #pragma unroll
-  for (int q = 0; q < WMAX; ++q) {
-    if (q < nsrc) {
-      const char* from = base + (row0 + src[q]) * row_stride;
+    for (int q = 0; q < WMAX; ++q) {
+      if (q < nsrc) {
+        const char* from = base + (row0 + src[q]) * row_stride;
 #pragma unroll
-      for (int k = 0; k < NP; ++k)
-        if (ok[k]) v[k][q] = *reinterpret_cast<const WT*>(from + off[k]);
+        for (int k = 0; k < NP; ++k)
+          if (ok[k]) v[k][q] = __builtin_nontemporal_load(reinterpret_cast<const WT*>(from + off[k]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < WMAX; ++q) {
+      if (q < nsrc) {
+        const char* from = base + (row0 + src[q]) * row_stride;
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+          if (ok[k]) v[k][q] = *reinterpret_cast<const WT*>(from + off[k]);
+      }
     }
   }
   // In place: a destination row may be another copy's parent. No other thread
@@ -81,6 +95,15 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
   }
 }
 
+// Parent reads. Plain loads let a launch reuse what the previous step's
+// launch left in the 256 MB Infinity Cache (the rows it wrote are often this
+// step's parents): at the Llama-3-8B shape, t = 50..100, they ran at 6.7-7.5
+// TB/s against 5.3-5.6 with the nontemporal hint. When the launch's region
+// (rows x positions x planes) is several times the cache nothing survives to
+// the next launch, and reads that do not allocate leave the launch's own
+// lines in place: 4.5-7% faster per launch at the wide shape, t >= 128. The
+// host sets stream_loads when that region exceeds 1 GiB.
+//
 // Work order. The hardware hands consecutive workgroups (x fastest, then y,
 // z) to the 8 XCDs in turn, so in grid order every XCD takes every eighth
 // tile of every row span. With whole_planes set (the launch's plane count a
@@ -136,10 +159,11 @@ __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
   // every word of the tile is in range (uniform), except in the last tile
   const int64_t e0 = (int64_t)bx * NP * kK3Threads + threadIdx.x;
   if ((int64_t)(bx + 1) * NP * kK3Threads <= a.words)
-    move_words<WMAX, WT, NP, true>(base, row0, a.row_stride, off, e0, a.words, nsrc, src, dmask);
+    move_words<WMAX, WT, NP, true>(base, row0, a.row_stride, off, e0, a.words, nsrc, src, dmask,
+                                   a.stream_loads);
   else
     move_words<WMAX, WT, NP, false>(base, row0, a.row_stride, off, e0, a.words, nsrc, src,
-                                    dmask);
+                                    dmask, a.stream_loads);
 }
 
 }  // namespace

@@ -644,6 +644,37 @@ def _kv_layout_case(dev, layout, W, timed):
     g.close()
 
 
+def test_kv_reorder_region_above_the_streaming_threshold(dev):
+    """A reorder whose region (rows x positions x planes) exceeds 1 GiB reads
+    its parents with the nontemporal hint: 16 rows x 1025 positions x 8 KiB x
+    8 planes = 1.07 GB, after a step that moves slots, against the oracle's
+    gather, bit for bit."""
+    import beam_search_step_amd as bs
+    B, W, V = 4, 4, 40
+    wl = synth.WORKLOADS["toy"].replace(batch=B, beam=W, vocab=V, eos_id=-1, stop="never",
+                                        lp="none", alpha=0.0, max_steps=3, seed=97)
+    g = bs.BeamSearch.for_workload(wl)
+    ref = oracle.Search.for_workload(wl)
+    for t in (1, 2):
+        lg = synth.logits(wl, t)
+        bi, tk, sc, dn = g.step(to_device(lg, dev))
+        obi, otk, osc, odn = ref.step(lg)
+    assert np.array_equal(bi.cpu().numpy(), obi)
+    moved = sum(int(obi[b, w] != w) for b in range(B) for w in range(W) if osc[b, w] > -np.inf)
+    assert moved > 0
+    gen, words, n_planes = 1025, 2048, 8
+    assert B * W * gen * words * 4 * n_planes > 2 ** 30
+    rng = np.random.default_rng(3)
+    host = [rng.integers(-2 ** 31, 2 ** 31 - 1, size=(B * W, gen, words), dtype=np.int64)
+            .astype(np.int32) for _ in range(n_planes)]
+    planes = [torch.from_numpy(h).to(dev) for h in host]
+    g.reorder_kv(planes, gen)
+    oracle.kv_reorder(host, obi, odn, gen)
+    for li, (p, h) in enumerate(zip(planes, host)):
+        assert np.array_equal(p.cpu().numpy(), h), f"plane {li} differs"
+    g.close()
+
+
 @pytest.mark.parametrize("name", sorted(PATTERNS))
 def test_kv_reorder_patterns(dev, name):
     import beam_search_step_amd as bs
