@@ -57,8 +57,12 @@
  * suite: the two-step tree of "llm_internals" Table 9-5, the length-penalty
  * Table 9-6, the blockwise Figure 1 example, exhaustive search over all |V|^n
  * paths on tiny inputs, W=1 against greedy argmax, and torch CPU
- * log_softmax/topk/index_select special cases. The exact stopping step of the
- * heuristic and "never" stop modes beyond hand-built cases is parity unpinned.
+ * log_softmax/topk/index_select special cases, and a search that never stops
+ * early: the "never" mode (any length penalty) and the heuristic mode (no
+ * length penalty) must return what that search reaches at the maximum length.
+ * The exact stopping step of both modes beyond hand-built cases, and the
+ * heuristic mode's result under a length penalty (where it may differ from the
+ * full search), are parity unpinned.
  */
 #include <math.h>
 #include <stdint.h>

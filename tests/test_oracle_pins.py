@@ -3,7 +3,8 @@
 Every test here runs on the CPU. Each one ties the oracle to a value printed on
 the pages (golden fixtures under tests/golden/, each citing its table or
 figure), a closed form, exhaustive search over all |V|^n paths, greedy argmax,
-or a torch CPU routine that computes a special case of the same step.
+a torch CPU routine that computes a special case of the same step, or a plain
+search without early stopping that the stop rules must not change.
 """
 import itertools
 import math
@@ -226,6 +227,73 @@ def test_exhaustive_with_eos_never_stop(orc, lp, alpha, seed):
         assert abs(nm[0, r] - norm[order[r]]) < 1e-5
 
 
+def lp_value(lp, alpha, L):
+    return {"none": 1.0, "gnmt": ((5 + L) / 6) ** alpha, "pow": L ** alpha}[lp]
+
+
+def search_without_stop(seed, V, W, T, eos, lp, alpha):
+    """Beam search that runs every step up to T, in double ("llm_internals"
+    9.2.2: each live sequence extended by every token, the best W of all
+    candidates kept, an EOS selection moved to the finished hypotheses; the
+    live sequences left at T join them). Returns the best W finished
+    (normalised score, tokens) pairs and the smallest gap between the W-th and
+    the (W+1)-th candidate over the steps, to reject near-tie seeds."""
+    beams = [((), 0.0)]
+    fin = []
+    gap = np.inf
+    for _ in range(T):
+        cands = []
+        for seq, s in beams:
+            lsm = lsm64(synth.prefix_logits(seed, seq, V))
+            cands += [(s + lsm[v], seq + (v,)) for v in range(V)]
+        cands.sort(key=lambda c: -c[0])
+        if len(cands) > W:
+            gap = min(gap, cands[W - 1][0] - cands[W][0])
+        beams = []
+        for c, seq in cands[:W]:
+            if seq[-1] == eos:
+                fin.append((c / lp_value(lp, alpha, len(seq)), seq))
+            else:
+                beams.append((seq, c))
+        if not beams:
+            break
+    fin += [(s / lp_value(lp, alpha, len(seq)), seq) for seq, s in beams]
+    fin.sort(key=lambda h: -h[0])
+    return fin[:W], gap
+
+
+@pytest.mark.parametrize("stop,lp,alpha", [("never", "none", 0.0), ("never", "gnmt", 0.6),
+                                           ("never", "gnmt", 1.5), ("never", "pow", 0.5),
+                                           ("heuristic", "none", 0.0)])
+def test_early_stop_leaves_the_result_unchanged(orc, stop, lp, alpha):
+    """The "never" rule ends an item only when no live sequence can still
+    enter the finished set, at any length up to the maximum (P1, batched
+    section: the early_stopping modes); without a length penalty scores only
+    fall, so the heuristic rule's test against the step's best score is safe
+    too. Either way the finished set must be the one a search that never
+    stops early reaches at the maximum length. Over many seeds the rule must
+    also end some searches well before it."""
+    V, W, T, eos = 5, 3, 9, 4
+    early = 0
+    checked = 0
+    for seed in range(40):
+        ref, gap = search_without_stop(seed, V, W, T, eos, lp, alpha)
+        norms = [h[0] for h in ref]
+        if gap < 1e-4 or (len(norms) > 1 and np.min(-np.diff(norms)) < 1e-4):
+            continue  # a near tie: fp32 and double may order it differently
+        o = run_prefix_search(orc, V, T, W, seed, eos=eos, lp=lp, alpha=alpha, stop=stop)
+        if o.done()[0] and o.steps < T:
+            early += 1
+        tok, ln, nm = o.finish(W)
+        got = [(float(nm[0, r]), tuple(tok[0, r, :ln[0, r]].tolist()))
+               for r in range(W) if ln[0, r] > 0]
+        assert [h[1] for h in got] == [h[1] for h in ref], f"seed {seed}: {got} vs {ref}"
+        np.testing.assert_allclose([h[0] for h in got], norms, rtol=0, atol=1e-5)
+        checked += 1
+    assert checked >= 30, f"only {checked} seeds free of near ties"
+    assert early >= 5, f"the rule ended only {early} of {checked} searches early"
+
+
 # ---------------------------------------------------------------------------
 # greedy, torch CPU special cases, step-1 initialisation
 # ---------------------------------------------------------------------------
@@ -354,6 +422,10 @@ def test_stop_never_hand_cases(orc):
     # best live -5.0/lp(9) = -3.007 cannot reach the worst kept: stop
     assert _run_stop(orc, [[E(-1.0), L(-1.5)], [E(-1.6), L(-5.0)]],
                      "never", "gnmt", 0.6) == [False, True]
+    # the bound takes the maximum length: -1.75/lp(9) = -1.053 can still beat
+    # the worst kept (-1.459), though -1.75/lp(3) = -1.473 could not: continue
+    assert _run_stop(orc, [[E(-1.0), L(-1.5)], [E(-1.6), L(-1.75)]],
+                     "never", "gnmt", 0.6) == [False, False]
 
 
 # ---------------------------------------------------------------------------
