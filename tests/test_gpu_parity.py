@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 import synth
-from parity import Report, compare_final, run_stepwise, same_float, to_device
+from parity import (Report, check_selection, compare_final, run_stepwise, same_float,
+                    to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -706,6 +707,49 @@ def test_kv_reorder_patterns(dev, name):
     else:
         assert osc[0, 3] == -np.inf and obi[0, 3] == 3   # dead slot keeps its row
     g.close()
+
+
+@pytest.mark.parametrize("stop,lp,alpha", [("never", "none", 0.0), ("never", "gnmt", 0.6),
+                                           ("never", "gnmt", 1.5), ("never", "pow", 0.5),
+                                           ("heuristic", "none", 0.0), ("heuristic", "gnmt", 0.6),
+                                           ("true", "gnmt", 0.6)])
+def test_stop_rules_on_a_prefix_model(dev, stop, lp, alpha):
+    """40 items, each a search of a toy model whose logits depend on the token
+    prefix (V = 5, W = 3, T = 9, EOS = 4), driven in lockstep with the oracle:
+    each step's logits come from the oracle's sequences; the library's ranked
+    selection must match the oracle's (near ties aside), the oracle then
+    applies it, and beam_idx, tokens, scores and done flags must be equal at
+    every step, the final hypotheses at the end. The items end at different
+    steps, so done items sit beside live ones."""
+    import beam_search_step_amd as bs
+    B, V, W, T, eos = 40, 5, 3, 9, 4
+    g = bs.BeamSearch(B, W, V, T, eos_id=eos, lp=lp, alpha=alpha, stop=stop, num_return=W)
+    ref = oracle.Search(B, W, V, T, eos_id=eos, lp=lp, alpha=alpha, stop=stop)
+    ended = np.full(B, T + 1)
+    rep = Report()
+    for t in range(T):
+        seqs = ref.seqs()
+        lg = np.stack([synth.prefix_logits(b, seqs[b, w, :t], V)
+                       for b in range(B) for w in range(W)])
+        bi, tk, sc, dn = (x.cpu().numpy() for x in g.step(torch.from_numpy(lg).to(dev)))
+        gj, gc = (x.cpu().numpy() for x in g.selection())
+        where = f"{stop} {lp} {alpha} step {t + 1}"
+        oj, oc, on = ref.select(lg)
+        for b in range(B):
+            check_selection((oj[b], oc[b], on[b]), lambda js, b=b: ref.cand_scores(lg, b, js),
+                            gj[b], gc[b], W, rep, f"{where} item {b}")
+        obi, otk, osc, odn = ref.apply(gj.astype(np.int64), gc)  # teacher forcing
+        assert np.array_equal(bi, obi), f"{where}: beam_idx"
+        assert np.array_equal(tk, otk), f"{where}: token_id"
+        assert np.array_equal(sc, osc), f"{where}: scores"
+        assert np.array_equal(dn.astype(bool), odn), f"{where}: done"
+        ended[odn & (ended > T)] = t + 1
+        if odn.all():
+            break
+    compare_final(g, ref, range(B), W, f"{stop} {lp} {alpha}")
+    g.close()
+    log(f"{stop} {lp} {alpha}: items ended at steps {np.bincount(ended, minlength=T + 2)[1:]}")
+    assert (ended <= T).any() and (ended > 1).all()
 
 
 def test_graph_capture_replays_match_eager(dev):
