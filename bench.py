@@ -452,9 +452,10 @@ def bench_verify(args, torch, bs, dev):
         out["roofline"] = {"bound": "hbm", "kernel": "k4_row (row segments) + k4_accept, one call",
                            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": ach / PEAK_HBM_GBS,
-                           # counters taken on the exact criterion (one call
-                           # of either kind reads the same logits)
-                           "traffic": measured_traffic("k4_verify", "verify") if exact else None,
+                           # counters of each criterion's kernels; top_k and
+                           # min_block enter only the accept step, so one
+                           # summary covers every top-k call
+                           "traffic": measured_traffic("k4_verify", "verify" if exact else "verify_topk"),
                            "alg_bytes_per_launch": alg, "avg_launch_us": 1e6 * d.mean()}
         out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
     # model calls per generated token implied by the mean accepted block k^
