@@ -7,12 +7,25 @@ with early stopping "true", 200 decode steps per search, KV cache 32 layers x
 8 KV heads x 128 dims bf16 (128 KiB per token per beam) behind a 1000-token
 prompt that is shared and never moved.
 
-One benchmark step is one decode step t of the search: bs_step (expand,
-score, prune, finalize over the [B*W, V] logits) followed by bs_reorder_kv
-with gen_len = t over the (layer, K|V) planes. Steps cycle through
-t = 1..max_steps; a new search starts (bs_reset) after max_steps steps.
+One benchmark step is one decode step t of a search: bs_step (expand, score,
+prune, finalize over the [B*W, V] logits) followed by bs_reorder_kv with
+gen_len = t over the (layer, K|V) planes.
+
+Which steps are timed. A search's steps differ widely in cost (the reorder
+moves t positions per moved row, so step 200 moves 200 times what step 1
+does), and a run of K steps must stand for the whole search. The K timed
+steps are one per stratum: the search's T steps split into K equal strata,
+and the i-th timed step is t_i = floor((2i+1) T / 2K) + 1, the middle of the
+i-th (t = 6, 16, ..., 196 for K = 20, T = 200; every step once for K = T).
+Each timed step runs on a search of its own (a handle with its own KV
+cache), brought to step t_i - 1 before the timed region by running steps 1 ..
+t_i - 1; so the timed region is K real decode steps issued back to back,
+whose mix is that of the whole search. No timed step finds in the caches
+what the previous timed step wrote (each search's KV cache is its own
+memory), as in a decoder whose model forward runs between two steps.
+
 Logits come from a pool of device buffers larger than the 256 MB Infinity
-Cache, filled with distinct seeded steps.
+Cache, filled with distinct seeded steps; step t reads buffer (t-1) mod pool.
 
 ``--workload tbase`` and ``--workload wide`` run the Transformer-base and
 wide-beam searches the same way; ``--workload verify`` times bs_verify on the
@@ -21,8 +34,13 @@ blockwise-parallel verify shape (B=64, k=8, V=32000 fp32).
 Output: one JSON line. ``value`` is steps/s over the timed steps with all
 inputs resident in HBM. ``roofline`` is for the dominant kernel (the KV
 reorder; for verify, the verify call): algorithmic bytes over launch
-durations measured with HIP events on the library's stream. ``cpu_baseline``
-times the CPU oracle on a bounded sample of the same workload.
+durations measured with HIP events on the library's stream, in a second pass
+of the same steps. ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the same workload.
+
+Profiling. The timed region (and the plain-copy reference) is bracketed by
+roctxProfilerResume(0) / roctxProfilerPause(0): ``rocprofv3
+--selected-regions`` then traces, or counts, exactly the timed launches.
 """
 from __future__ import annotations
 
@@ -47,12 +65,20 @@ METRIC = "beam steps/sec and achieved HBM GB/s (% of peak) at B,W,V; 1 GPU"
 # pool holds every step of a search.
 POOLS = {"llama3_8b": (64, 16), "tbase": (128, 128), "wide": (3, 3)}
 
+# device memory for the searches' KV caches: one region per timed step while
+# they fit, else a ring of full-length regions (consecutive timed steps
+# always use different regions)
+KV_BUDGET_BYTES = 64 << 30
+
 
 def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed decode steps, one per stratum of the search (the search's "
+                         "length: every step once)")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed decode steps first, on a search of their own")
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "tbase", "wide", "verify"])
     ap.add_argument("--prune", default="topw", choices=["topw", "top2w"],
@@ -83,13 +109,45 @@ def parse(argv=None):
                          "steps after the timed region: 0 none; 1 HIP events attached to the "
                          "reorder's kernel dispatches (contiguous KV; the paged cache takes 2); 2 "
                          "an event pair recorded around every reorder call")
-    ap.add_argument("--graph", type=int, default=0, choices=[0, 1],
-                    help="also time the K steps replayed from one HIP graph captured on the "
-                         "library's stream (no host issue cost per launch); value is then the "
-                         "graph's rate")
     ap.add_argument("--copy-reference", type=int, default=1,
                     help="time a plain 1 GiB device copy after the timed region")
     return ap.parse_args(argv)
+
+
+def schedule(k, steps_per_search):
+    """The step numbers of k timed steps, one per stratum: the search's
+    steps 1..T split into k equal strata, t_i = floor((2i+1) T / 2k) + 1."""
+    T = steps_per_search
+    return [(2 * i + 1) * T // (2 * k) + 1 for i in range(k)]
+
+
+class ProfilerRegion:
+    """roctxProfilerResume(0) / roctxProfilerPause(0) around the timed work,
+    for ``rocprofv3 --selected-regions``; without a profiler they do nothing.
+    Absent where the ROCm profiler library is not installed."""
+
+    def __init__(self):
+        self.lib = None
+        path = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib",
+                            "librocprofiler-sdk-roctx.so.1")
+        try:
+            lib = ctypes.CDLL(path)
+        except OSError:
+            return
+        for name in ("roctxProfilerResume", "roctxProfilerPause"):
+            getattr(lib, name).argtypes = [ctypes.c_uint64]
+            getattr(lib, name).restype = ctypes.c_int
+        self.lib = lib
+
+    def __enter__(self):
+        if self.lib:
+            self.lib.roctxProfilerResume(0)
+        return self
+
+    def __exit__(self, *exc):
+        if self.lib:
+            self.lib.roctxProfilerPause(0)
+        return False
 
 
 def main(argv=None):
@@ -99,6 +157,9 @@ def main(argv=None):
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the beam-step "
                                    "library has no multi-GPU path", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
+        sys.exit(2)
 
     import torch
     import beam_search_step_amd as bs
@@ -106,16 +167,17 @@ def main(argv=None):
     bs.library()  # fail loudly if the HIP library is not built
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    region = ProfilerRegion()
     if args.workload == "verify":
-        out = bench_verify(args, torch, bs, dev)
+        out = bench_verify(args, torch, bs, dev, region)
     else:
-        out = bench_search(args, torch, bs, dev)
+        out = bench_search(args, torch, bs, dev, region)
     if args.copy_reference:
-        out["copy_reference"] = copy_reference(torch, dev)
+        out["copy_reference"] = copy_reference(torch, dev, region)
     print(json.dumps(out))
 
 
-def bench_search(args, torch, bs, dev):
+def bench_search(args, torch, bs, dev, region):
     import synth
 
     wl = synth.WORKLOADS[args.workload]
@@ -126,6 +188,8 @@ def bench_search(args, torch, bs, dev):
     bpp = wl.kv_bytes_per_pos
     if wl.name == "llama3_8b":
         assert W * V == 513024 and wl.kv_bytes_per_token == 131072
+    K = args.steps
+    ts = schedule(K, T)
     pool_n, distinct_n = POOLS[wl.name]
     # at any batch, enough buffers for twice the 256 MB Infinity Cache
     pool_n = max(pool_n, -(-512_000_000 // (wl.rows * V * wl.elem_bytes)))
@@ -142,153 +206,176 @@ def bench_search(args, torch, bs, dev):
         for i in range(s, pool_n, distinct_n):
             pool[i].copy_(src)
     gen_s = time.time() - t0
-    # the library's stream: a stream of its own when the steps are captured
-    # into a graph (the legacy default stream cannot be captured)
-    lib_stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
-    g = bs.BeamSearch.for_workload(wl, prune=args.prune, tile_elems=args.tile_elems,
-                                   select=args.select, stream=lib_stream)
+
+    stream = torch.cuda.current_stream()
+    kw = dict(prune=args.prune, tile_elems=args.tile_elems, select=args.select)
+    # one search per timed step, and one for the warmup
+    searches = [bs.BeamSearch.for_workload(wl, **kw) for _ in range(K)]
+    warm = bs.BeamSearch.for_workload(wl, **kw)
     paged = args.kv == "paged"
     bsz = args.block_size
+    words = bpp // 4
     if paged:
-        pk = bs.PagedKV(g, bsz)
-        kv = [torch.zeros((B * pk.blocks_per_item, bsz, bpp // 4), dtype=torch.int32, device=dev)
-              for _ in range(planes_n)]
-        desc = bs.make_kv_pool(kv)
+        # block tables are search state: every search has its own cache
+        pks = [bs.PagedKV(g, bsz) for g in searches + [warm]]
+        pk0 = pks[0]
+        pool_bytes = planes_n * B * pk0.blocks_per_item * bsz * bpp
+        if pool_bytes * (K + 1) > 4 * KV_BUDGET_BYTES:
+            raise SystemExit(f"--kv paged: {K + 1} block pools of {pool_bytes / 2**30:.1f} GiB "
+                             f"do not fit; time fewer steps")
+        kv_mem = [torch.zeros((planes_n, B * pk0.blocks_per_item, bsz, words), dtype=torch.int32,
+                              device=dev) for _ in range(K + 1)]
+        descs = [bs.make_kv_pool(list(m)) for m in kv_mem]
+        kv_h = [p.h for p in pks]
+        region_of = list(range(K + 1))
     else:
-        kv = [torch.zeros((wl.rows, T, bpp // 4), dtype=torch.int32, device=dev)
-              for _ in range(planes_n)]
-        desc = bs.make_kv_desc(kv, pos_offset=0)
-    n_hist = args.steps
-    hist_bi = torch.empty((n_hist, B, W), dtype=torch.int32, device=dev)
-    hist_tk = torch.empty_like(hist_bi)
-    hist_sc = torch.empty((n_hist, B, W), dtype=torch.float32, device=dev)
-    hist_dn = torch.empty((n_hist, B), dtype=torch.uint8, device=dev)
-    stream = lib_stream
+        per_pos = planes_n * wl.rows * bpp
+        if sum(ts) * per_pos <= KV_BUDGET_BYTES:
+            kv_mem = [torch.zeros((planes_n, wl.rows, t, words), dtype=torch.int32, device=dev)
+                      for t in ts]
+            region_of = list(range(K))
+        else:
+            n_reg = int(max(2, min(K, KV_BUDGET_BYTES // (T * per_pos))))
+            kv_mem = [torch.zeros((planes_n, wl.rows, T, words), dtype=torch.int32, device=dev)
+                      for _ in range(n_reg)]
+            region_of = [i % n_reg for i in range(K)]
+        # the warmup search: its own region of min(warmup, T) positions
+        kv_mem.append(torch.zeros((planes_n, wl.rows, max(1, min(args.warmup, T)), words),
+                                  dtype=torch.int32, device=dev))
+        region_of.append(len(kv_mem) - 1)
+        descs = [bs.make_kv_desc(list(m), pos_offset=0) for m in kv_mem]
+        kv_h = [g.h for g in searches + [warm]]
 
-    # events are created before the timed region, one pair per step of the
-    # second pass: either attached to the reorder's kernel dispatch (mode 1,
-    # bs_reorder_kv_timed), so that they take the kernel's own start and end,
-    # or recorded around the reorder call (mode 2)
+    # per timed step: its outputs, and the outputs of its search's step
+    # t_i - 1 (the state the step starts from)
+    hist = [torch.empty((K, B, W), dtype=torch.int32, device=dev) for _ in range(2)] + \
+           [torch.empty((K, B, W), dtype=torch.float32, device=dev),
+            torch.empty((K, B), dtype=torch.uint8, device=dev)]
+    prev = [torch.empty_like(x) for x in hist]
+    scratch = [x[0].clone() for x in hist]
+    ptrs = lambda xs, i: tuple(x[i].data_ptr() for x in xs)  # noqa: E731
+    hist_ptrs = [ptrs(hist, i) for i in range(K)]
+    prev_ptrs = [ptrs(prev, i) for i in range(K)]
+    scratch_ptrs = tuple(x.data_ptr() for x in scratch)
+
     ev_mode = 2 if (paged and args.events == 1) else args.events
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps if ev_mode else 0)]
+              for _ in range(K if ev_mode else 0)]
     for e0, e1 in events:  # the handles exist once recorded
         e0.record(stream)
         e1.record(stream)
     torch.cuda.synchronize()
     ev_ptrs = [(e0.cuda_event, e1.cuda_event) for e0, e1 in events]
-    hist = [(hist_bi[i], hist_tk[i], hist_sc[i], hist_dn[i]) for i in range(n_hist)]
 
-    # the timed loop calls the C entry points directly, with every pointer
-    # computed beforehand, so that the host issues a step in a few
-    # microseconds: the early steps of a search take the GPU less time than
-    # the Python wrappers would take to issue them
+    # the loops call the C entry points directly, with every pointer computed
+    # beforehand, so that the host issues a step in a few microseconds: the
+    # early steps of a search take the GPU less time than the Python wrappers
+    # would take to issue them
     L = bs.library()
-    h = g.h
-    ph = pk.h if paged else None
     pool_ptrs = [pool[i].data_ptr() for i in range(pool_n)]
     row_stride = pool.stride(1)
-    hist_ptrs = [tuple(x.data_ptr() for x in o) for o in hist]
-    desc_ref = ctypes.byref(desc)
-    step_c, kv_c = L.bs_step, (L.bs_kv_paged_reorder if paged else L.bs_reorder_kv)
+    desc_refs = [ctypes.byref(d) for d in descs]
+    step_c = L.bs_step
+    kv_c = L.bs_kv_paged_reorder if paged else L.bs_reorder_kv
     kv_timed = L.bs_reorder_kv_timed
-    kv_h = ph if paged else h
-    taken = [0]  # steps of the current search (the library's own count)
 
-    def reset():
+    def call(rc, what):
+        if rc:
+            raise bs.BeamStepError(rc, what)
+
+    def reorder(i, t, with_events=0, ev=None):
+        """The reorder of search i (len(searches) = the warmup search)."""
+        d = desc_refs[region_of[i]]
+        if with_events == 1:
+            call(kv_timed(kv_h[i], d, t, *ev), "bs_reorder_kv_timed")
+        else:
+            call(kv_c(kv_h[i], d, t), "reorder")
+
+    def prepare(i):
+        """Search i from a reset to step ts[i] - 1. The contiguous cache of a
+        benchmark search holds zeros, which a reorder leaves as they are, so
+        its reorders are not run here; the paged cache's block tables are
+        search state, so they are."""
+        g = searches[i]
         g.reset()
         if paged:
-            pk.reset()
-        taken[0] = 0
+            pks[i].reset()
+        for t in range(1, ts[i]):
+            o = prev_ptrs[i] if t == ts[i] - 1 else scratch_ptrs
+            call(step_c(g.h, pool_ptrs[(t - 1) % pool_n], row_stride, *o), "bs_step")
+            if paged:
+                reorder(i, t)
 
-    def run(n, record, with_events=0):
-        ts = []
-        for i in range(n):
-            t = taken[0] % T + 1
-            if t == 1 and taken[0]:
-                reset()
-            o = hist_ptrs[i] if record else hist_ptrs[0]
-            rc = step_c(h, pool_ptrs[(t - 1) % pool_n], row_stride, *o)
-            if rc:
-                raise bs.BeamStepError(rc, "bs_step")
+    def run(with_events):
+        """The K timed steps, issued back to back."""
+        for i, t in enumerate(ts):
+            call(step_c(searches[i].h, pool_ptrs[(t - 1) % pool_n], row_stride, *hist_ptrs[i]),
+                 "bs_step")
             if with_events == 2:
                 events[i][0].record(stream)
-            if with_events == 1:
-                rc = kv_timed(kv_h, desc_ref, t, *ev_ptrs[i])
-            else:
-                rc = kv_c(kv_h, desc_ref, t)
-            if rc:
-                raise bs.BeamStepError(rc, "reorder")
+            reorder(i, t, with_events, ev_ptrs[i] if with_events == 1 else None)
             if with_events == 2:
                 events[i][1].record(stream)
-            taken[0] = t
-            ts.append(t)
-        return ts
 
-    def timed(with_events):
-        """The same K steps from a fresh search: wall time, the step numbers
-        run and the algorithmic bytes of every step."""
-        reset()
+    # warmup: the first steps of a search of its own (untimed)
+    warm_i = len(searches)
+    for n in range(args.warmup):
+        t = n % T + 1
+        if t == 1:
+            warm.reset()
+            if paged:
+                pks[warm_i].reset()
+        call(step_c(warm.h, pool_ptrs[(t - 1) % pool_n], row_stride, *scratch_ptrs), "bs_step")
+        reorder(warm_i, min(t, kv_mem[region_of[warm_i]].shape[2]) if not paged else t)
+
+    # the timed region: K steps, no events (an event record stalls the GPU for
+    # several microseconds between kernels)
+    for i in range(K):
+        prepare(i)
+    torch.cuda.synchronize()
+    with region:
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        ts = run(args.steps, True, with_events)
+        run(0)
         torch.cuda.synchronize()
-        return ts, time.perf_counter() - t_start, alg_bytes(ts)
-
-    def timed_graph():
-        """The same K steps, from a fresh search, captured once into a HIP
-        graph on the library's stream and replayed: the GPU runs the same
-        launches with the same arguments, without the host's issue cost."""
-        graph = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=lib_stream):
-            reset()
-            ts = run(args.steps, True, 0)
-        graph.replay()  # untimed
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        return ts, time.perf_counter() - t_start, alg_bytes(ts)
+        elapsed = time.perf_counter() - t_start
 
     # ---- algorithmic bytes from the recorded step outputs -----------------------
-    def alg_bytes(ts):
-        bi = hist_bi.cpu().numpy()
-        sc = hist_sc.cpu().numpy()
-        dn = hist_dn.cpu().numpy().astype(bool)
-        kv_b, logit_b = step_bytes(ts, bi, sc, dn)
-        return kv_b, logit_b, int((~dn).sum())
+    def recorded(xs):
+        return [x.cpu().numpy() for x in xs]
 
-    kv_rw = [0, 0]  # KV bytes read (distinct parents) and written (moved slots)
+    bi, tk, sc, dn = recorded(hist)
+    _, _, psc, pdn = recorded(prev)
+    paged_geom = (bsz, pk0.max_blocks, pk0.blocks_per_item) if paged else None
+    kv_bytes, logit_bytes, kv_read, kv_written = algorithmic_bytes(
+        ts, bi, sc, dn.astype(bool), V, wl.elem_bytes, bpp, planes_n, paged=paged_geom,
+        prev=(psc, pdn.astype(bool)))
+    live_item_steps = int((~dn.astype(bool)).sum())
 
-    def step_bytes(ts, bi, sc, dn):
-        kv, lb, kv_rw[0], kv_rw[1] = algorithmic_bytes(
-            ts, bi, sc, dn, V, wl.elem_bytes, bpp, planes_n,
-            paged=(bsz, pk.max_blocks, pk.blocks_per_item) if paged else None)
-        return kv, lb
-
-    # warmup (untimed); the timed region, which uses no events: an event
-    # record stalls the GPU for several microseconds between kernels, and
-    # events attached to a dispatch slow every step by more; then, for the
-    # per-launch durations, the same K steps with a pair of events per reorder
-    reset()
-    run(args.warmup, False)
-    ts, elapsed, (kv_bytes, logit_bytes, live_item_steps) = timed(0)
-    eager_elapsed = elapsed
-    if args.graph:
-        ts_g, elapsed, (kv_bytes_g, _, _) = timed_graph()
-        assert ts_g == ts and np.array_equal(kv_bytes_g, kv_bytes), "graph replay differs"
+    # the events pass: the same K steps from the same states, with HIP events
+    # for every reorder launch's duration
     if ev_mode:
-        _, elapsed_ev, (kv_bytes_ev, logit_bytes_ev, _) = timed(ev_mode)
+        for i in range(K):
+            prepare(i)
+        torch.cuda.synchronize()
+        t_ev = time.perf_counter()
+        run(ev_mode)
+        torch.cuda.synchronize()
+        elapsed_ev = time.perf_counter() - t_ev
+        bi2, _, sc2, dn2 = recorded(hist)
+        assert np.array_equal(bi2, bi) and np.array_equal(sc2, sc) and np.array_equal(dn2, dn), \
+            "the events pass ran different steps"
 
+    where = "t = " + (", ".join(map(str, ts)) if K <= 8 else
+                      f"{ts[0]}, {ts[1]}, ..., {ts[-1]}")
     out = {
         "metric": METRIC,
-        "value": args.steps / elapsed,
+        "value": K / elapsed,
         "unit": "beam steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": 1e3 * elapsed / args.steps,
+        "ms_per_step": 1e3 * elapsed / K,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -297,38 +384,38 @@ def bench_search(args, torch, bs, dev):
         "config": {
             "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
                         f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
-                        f"gen_len = t" + (", 2W-candidate fill" if args.prune == "top2w" else "")
+                        f"gen_len = t; the {K} timed steps are one per stratum of the {T}-step "
+                        f"search ({where}), each on a search of its own brought to step t-1 "
+                        f"outside the timed region"
+                        + (", 2W-candidate fill" if args.prune == "top2w" else "")
                         + (", two-pass selection" if args.select == "two_pass" else "")
                         + (f", paged KV (blocks of {bsz} positions, copy on write)" if paged else ""),
             "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype, "prune": args.prune,
             "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
-            "logit_pool_buffers": pool_n, "kv": args.kv, "select": args.select,
-            **({"block_size": bsz} if paged else {}),
+            "timed_steps": ts, "logit_pool_buffers": pool_n, "kv": args.kv,
+            "select": args.select, **({"block_size": bsz} if paged else {}),
         },
         "alg_gbs_whole_step": (kv_bytes.sum() + logit_bytes.sum()) / elapsed / 1e9,
-        "launch": "one HIP graph of the timed steps, replayed" if args.graph
-                  else "the C entry points called from the host, step by step",
-        **({"eager_value": args.steps / eager_elapsed} if args.graph else {}),
+        "launch": "the C entry points called from the host, step by step",
         "live_item_steps": live_item_steps,
-        **({} if paged else {"kv_read_write_bytes": list(kv_rw)}),
+        **({} if paged else {"kv_read_write_bytes": [kv_read, kv_written]}),
     }
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if ev_mode:
         d_kv = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
-        # between one step's reorder and the next: bs_step's two kernels
+        # between one step's reorder and the next: the next step's bs_step
         d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
                            for i in range(1, len(events))]) * 1e-3
-        ach = kv_bytes_ev.sum() / d_kv.sum() / 1e9
-        step_gbs = logit_bytes_ev[1:].sum() / d_step.sum() / 1e9
-        # the reorder over a search: mean duration and rate of its launches at
-        # a few steps t (every search of the pass that reached that step)
+        ach = kv_bytes.sum() / d_kv.sum() / 1e9
+        step_gbs = logit_bytes[1:].sum() / d_step.sum() / 1e9 if K > 1 else None
+        # the reorder at a few points of the search: the timed steps nearest
+        # to t = 1, T/4, T/2, 3T/4 and T
         tsa = np.array(ts)
         curve = {}
-        for tq in sorted({1, T // 4, T // 2, 3 * T // 4, T}):
-            sel = tsa == tq
-            if sel.any() and d_kv[sel].sum() > 0:
-                curve[str(tq)] = {"us": 1e6 * d_kv[sel].mean(),
-                                  "GBs": kv_bytes_ev[sel].sum() / d_kv[sel].sum() / 1e9}
+        for tq in (1, T // 4, T // 2, 3 * T // 4, T):
+            i = int(np.argmin(np.abs(tsa - tq)))
+            if d_kv[i] > 0:
+                curve[str(ts[i])] = {"us": 1e6 * d_kv[i], "GBs": kv_bytes[i] / d_kv[i] / 1e9}
         out["reorder_by_step"] = curve
         if paged:
             # the logits pass dominates once the reorder moves only partial blocks;
@@ -337,48 +424,50 @@ def bench_search(args, torch, bs, dev):
             out["roofline"] = {
                 "bound": "hbm", "kernel": "k1_expand_select + k2_select_finalize_paged",
                 "achieved": step_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": step_gbs / PEAK_HBM_GBS, "traffic": None,
-                "alg_bytes_per_launch": logit_bytes_ev.mean(), "avg_launch_us": 1e6 * d_step.mean(),
+                "frac": step_gbs / PEAK_HBM_GBS if step_gbs else None, "traffic": None,
+                "alg_bytes_per_launch": logit_bytes.mean(),
+                "avg_launch_us": 1e6 * d_step.mean() if K > 1 else None,
             }
             out["paged_reorder"] = {
                 "kernels": "k7_paged_copy", "avg_us": 1e6 * d_kv.mean(),
-                "alg_bytes_per_step": kv_bytes_ev.mean(), "alg_gbs": ach,
+                "alg_bytes_per_step": kv_bytes.mean(), "alg_gbs": ach,
             }
         else:
+            # (the selection algorithm and tile size do not change the result)
+            default_run = args.prune == "topw" and not (args.batch or args.pool or args.distinct)
             out["roofline"] = {
                 "bound": "hbm", "kernel": "k3_kv_reorder", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                # the counters were taken on the default run (top-W, the
-                # workload's own batch and logit pool); other runs change the
-                # reorder's bytes
-                "traffic": measured_traffic("k3_kv_reorder", wl.name, args.steps, T)
-                           if args.prune == "topw" and not (args.batch or args.pool
-                                                            or args.distinct) else None,
-                "alg_bytes_per_launch": kv_bytes_ev.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
+                # counters taken on this workload's default run with the same
+                # timed steps (the mean per launch depends on which steps ran)
+                "traffic": measured_traffic("k3_kv_reorder", wl.name, ts) if default_run else None,
+                "alg_bytes_per_launch": kv_bytes.mean(), "avg_launch_us": 1e6 * d_kv.mean(),
             }
-        out["step_kernels"] = {
-            # in the events pass, so it includes what the events cost between
-            # the kernels; the kernel trace gives k1 and k2 themselves
-            "kernels": "k1_expand_select + k2 (gap between reorders, events pass)",
-            "avg_us": 1e6 * d_step.mean(),
-            "alg_gbs": step_gbs,
-        }
+        if K > 1:
+            out["step_kernels"] = {
+                # in the events pass, so it includes what the events cost between
+                # the kernels; the kernel trace gives k1 and k2 themselves
+                "kernels": "k1_expand_select + k2 (gap between reorders, events pass)",
+                "avg_us": 1e6 * d_step.mean(),
+                "alg_gbs": step_gbs,
+            }
         out["launch_timing"] = ("events attached to the reorder's dispatches" if ev_mode == 1
                                 else "event records around each reorder call")
         # the events pass: the same steps, slower by the events' stalls
-        out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / args.steps
+        out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / K
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
     if paged:
-        ov, _ = pk.status()
-        out["paged_overflow"] = bool(ov)
-        pk.close()
-    g.close()
+        out["paged_overflow"] = any(bool(p.status()[0]) for p in pks)
+        for p in pks:
+            p.close()
+    for g in searches + [warm]:
+        g.close()
     return out
 
 
-def bench_verify(args, torch, bs, dev):
+def bench_verify(args, torch, bs, dev, region):
     """Blockwise-parallel verify: one step is one bs_verify call on [64, 8, 32000]
     fp32 logits (65.5 MB) from a pool of 8 distinct buffers."""
     import synth
@@ -432,7 +521,8 @@ def bench_verify(args, torch, bs, dev):
 
     # the timed region records no events (each record stalls the GPU for
     # several microseconds); a second pass brackets every call with events
-    elapsed = timed(False)
+    with region:
+        elapsed = timed(False)
     elapsed_ev = timed(True) if args.events else None
     alg = Bv * k * V * 4 + Bv * k * 4 * 2 + Bv * 4
     out = {
@@ -488,19 +578,22 @@ def bench_verify(args, torch, bs, dev):
     return out
 
 
-def algorithmic_bytes(ts, bi, sc, dn, V, elem_bytes, bpp, planes, paged=None):
+def algorithmic_bytes(ts, bi, sc, dn, V, elem_bytes, bpp, planes, paged=None, prev=None):
     """The HBM bytes each step of a run must move, from its recorded outputs.
 
-    ts: the step t of every run step (t = 1 starts a search); bi, sc, dn: the
-    step's beam_idx [B, W], scores [B, W] and done [B] as bs_step returned
-    them. A step reads the logits of the rows live before it (slot 0 of each
-    item at t = 1), plus 20 bytes of state and outputs per row. The contiguous
-    reorder reads each distinct parent of the moved slots once and writes each
-    moved slot (a live slot whose parent is another slot), t positions of
-    bpp bytes in every plane, for items not done after the step. The paged
-    reorder (paged = (block_size, max_blocks, blocks_per_item)) reads and
-    writes t % block_size positions for every live slot beyond the first child
-    of its parent, plus the items' tables, reference counts and free lists.
+    ts: the step t of every run step; bi, sc, dn: the step's beam_idx [B, W],
+    scores [B, W] and done [B] as bs_step returned them. prev: the scores and
+    done flags [n, B, W], [n, B] of each run step's own previous step (its
+    step t - 1 on the same search), or None when the run steps are consecutive
+    steps of one search (t = 1 starting a new one). A step reads the logits of
+    the rows live before it (slot 0 of each item at t = 1), plus 20 bytes of
+    state and outputs per row. The contiguous reorder reads each distinct
+    parent of the moved slots once and writes each moved slot (a live slot
+    whose parent is another slot), t positions of bpp bytes in every plane,
+    for items not done after the step. The paged reorder (paged =
+    (block_size, max_blocks, blocks_per_item)) reads and writes t % block_size
+    positions for every live slot beyond the first child of its parent, plus
+    the items' tables, reference counts and free lists.
     Returns (KV bytes per step, logit bytes per step, KV bytes read, KV bytes
     written), the last two for the contiguous reorder only."""
     n, B, W = bi.shape
@@ -511,6 +604,8 @@ def algorithmic_bytes(ts, bi, sc, dn, V, elem_bytes, bpp, planes, paged=None):
         if t == 1:
             prev_live = np.zeros((B, W), bool)
             prev_live[:, 0] = True
+        elif prev is not None:
+            prev_live = (prev[0][i] > -np.inf) & ~prev[1][i][:, None]
         logit_bytes.append(int(prev_live.sum()) * V * elem_bytes + 20 * B * W)
         if paged:
             bsz, max_blocks, bpi = paged
@@ -540,20 +635,23 @@ def algorithmic_bytes(ts, bi, sc, dn, V, elem_bytes, bpp, planes, paged=None):
             kv_read, kv_written)
 
 
-def copy_reference(torch, dev):
+def copy_reference(torch, dev, region=None):
     """A plain device copy of 1 GiB (torch's copy kernel): the practical
-    read+write HBM rate of this GPU, for comparison with the KV reorder."""
+    read+write HBM rate of this GPU, for comparison with the KV reorder, and
+    the calibration of the HBM counters (inside the profiled region)."""
     n = 1 << 30
     a = torch.empty(n // 2, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
     for _ in range(2):
         b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        b.copy_(a)
-    e1.record()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with region or ProfilerRegion():
+        e0.record()
+        for _ in range(5):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / 5
     return {"bytes_read_plus_written": 2 * n, "avg_us": us, "GBs": 2 * n / us / 1e3}
 
@@ -574,13 +672,13 @@ def kernel_source_hash(kernel):
     return hashlib.sha256(src[src.index(marker):].encode()).hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload, steps=None, steps_per_search=None):
+def measured_traffic(kernel, workload, timed_steps=None):
     """HBM bytes per launch (per call, for verify) from the committed
     rocprofv3 counter summary of this kernel and workload (FETCH_SIZE +
     WRITE_SIZE, each scaled by a plain copy's reading), or None: when there is
-    none for the current kernel, or when this run's steps are not the counted
-    ones (a search's launches move more KV as t grows, so the mean per launch
-    depends on which steps were run; whole searches all have the same mean)."""
+    none for the current kernel, or when this run's timed steps are not the
+    counted ones (a search's launches move more KV as t grows, so the mean per
+    launch depends on which steps were timed)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
         with open(path) as f:
@@ -589,11 +687,8 @@ def measured_traffic(kernel, workload, steps=None, steps_per_search=None):
         return None
     if d.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
-    if steps_per_search is not None:
-        counted = d.get("steps")
-        whole = counted and steps % steps_per_search == 0 and counted % steps_per_search == 0
-        if steps != counted and not whole:
-            return None
+    if timed_steps is not None and d.get("timed_steps") != list(timed_steps):
+        return None
     return d.get("bytes_per_launch", d.get("bytes_per_call"))
 
 
@@ -608,8 +703,9 @@ def cpu_baseline(wl, seconds, bpp, planes_n, prune="topw"):
     """The CPU oracle, single-threaded on one core, on a bounded sample: decode
     steps 1, 2, ... of the same search (select + apply over all items), each
     followed by the oracle's KV gather over every plane at gen_len =
-    max_steps / 2 (the mean gen_len of a full search), until ``seconds`` of
-    oracle time are spent. Each step's logits are generated outside the timing."""
+    max_steps / 2 (the mean gen_len of a full search; the selection's cost
+    does not depend on t once every row is live), until ``seconds`` of oracle
+    time are spent. Each step's logits are generated outside the timing."""
     import oracle
     import synth
 

@@ -19,9 +19,15 @@
  *   - Every call is enqueued on the handle's HIP stream and returns without
  *     waiting for the GPU, except where stated. Results are valid once the
  *     stream reaches them.
- *   - Every call returns a bs_status. Arguments are validated before any work
- *     is enqueued; a call that returns an error has enqueued nothing and left
- *     the handle unchanged. BS_EDEVICE reports a HIP error seen at launch.
+ *   - Every call returns a bs_status. BS_EINVAL and BS_ESTATE are decided on
+ *     the host before anything is enqueued: such a call has enqueued nothing
+ *     and left the handle unchanged. BS_EDEVICE reports a HIP error seen at a
+ *     launch. The launches the same call issued before that one may already
+ *     be enqueued (bs_step's first kernel, the earlier plane groups of a KV
+ *     reorder, a paged reorder's table update), so after BS_EDEVICE the
+ *     handle's search state and every buffer the call writes (outputs, KV
+ *     planes or pools) are undefined: bs_reset the handle and rebuild the
+ *     cache before using them again.
  *   - A handle is not thread-safe; use one handle per stream.
  *   - Logits must not contain NaN or +inf (behaviour is undefined); -inf is
  *     allowed and means "impossible token".
@@ -142,8 +148,11 @@ int bs_reset(bs_state *h);
  *            with |y| = t; every other selection becomes the next live slot.
  *            Live slots are compacted in rank order; remaining slots are dead
  *            (score -inf). Then the stop rule runs (see bs_stop).
- * Rows of items that are done, and dead rows (score -inf), are not read, so
- * their logits may hold anything.
+ * Rows of items that are done, and dead rows (score -inf), take no part in
+ * the step, whatever they hold (NaN included); their tiles are still loaded,
+ * because a tile's loads are issued together with its row's state so that a
+ * live row never waits for that state. Every row of the buffer must
+ * therefore be readable device memory.
  *   logits           device, [B*W][row_stride_elems] of fp32 or bf16 (as
  *                    configured); row r = b*W + w; only the first V of each
  *                    row are read

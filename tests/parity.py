@@ -84,8 +84,27 @@ def kv_position(wl, b, slot, pos, plane, words):
     return synth.kv_fill_values(b, slot, pos, plane, words).view(np.int32)
 
 
+def device_filler(wl, dev):
+    """Logits for the rows no oracle follows, drawn on the GPU: sigma * N(0, 1)
+    plus the workload's Zipf term, in its storage type. Items are independent
+    searches, so these rows only keep the launches at their full size."""
+    import torch
+    gen = torch.Generator(device=dev)
+    v = torch.arange(wl.vocab, dtype=torch.float32, device=dev)
+    bias = -wl.zipf_s * torch.log1p(v) if wl.zipf_s else torch.zeros_like(v)
+
+    def fill(t):
+        gen.manual_seed(wl.seed * 100003 + t)
+        x = torch.randn((wl.rows, wl.vocab), generator=gen, device=dev) * wl.sigma + bias
+        if wl.dtype == "bf16":
+            return x.to(torch.bfloat16).view(torch.int16)
+        return x
+    return fill
+
+
 def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_finished=True,
-                 rep=None, tile_elems=0, prune="topw", select="fused"):
+                 rep=None, tile_elems=0, prune="topw", select="fused", other_rows="synth",
+                 kv_check_every=1):
     """Run ``steps`` decode steps of workload ``wl`` on the GPU with the oracle
     following along on ``items`` (default: all; items are independent, so a
     sample of them can be followed at full batch size). With ``kv_planes`` > 0
@@ -94,31 +113,46 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     reordered with gen_len = t each step, and compared bit for bit on the
     followed items. ``prune`` picks the top-W or the 2W-candidate variant on
     both sides; ``select`` the library's selection algorithm (the oracle has
-    one). Returns (Report, gpu search, oracle search)."""
+    one). ``other_rows="device"`` generates only the followed items' logits on
+    the host (the workload's generator) and draws the other rows on the GPU
+    (``device_filler``); ``kv_check_every`` compares the followed rows' KV
+    every that many steps (and at the last). Returns (Report, gpu search,
+    oracle search)."""
     import torch
     import beam_search_step_amd as bs
 
     items = list(range(wl.batch)) if items is None else list(items)
-    logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     rep = rep or Report()
     W = wl.beam
     gpu = bs.BeamSearch.for_workload(wl, tile_elems=tile_elems, prune=prune, select=select)
     ref = oracle.Search.for_workload(wl.replace(batch=len(items)), prune=prune)
     K = gpu.K
     rows = np.array([b * W + w for b in items for w in range(W)])
+    rows_dev = torch.from_numpy(rows).to(dev)
     sub = np.array(items)
+    if other_rows == "device":
+        assert logits_fn is None
+        fill = device_filler(wl, dev)
+    else:
+        logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     words = wl.kv_bytes_per_pos // 4
     planes = [torch.zeros((wl.rows, steps, words), dtype=torch.int32, device=dev)
               for _ in range(kv_planes)]
     host = [np.zeros((len(rows), steps, words), np.int32) for _ in range(kv_planes)]
     for t in range(1, steps + 1):
         where = f"{wl.name} t={t}"
-        lg = logits_fn(t)
-        bi, tk, sc, dn = gpu.step(to_device(lg, dev))
+        if other_rows == "device":
+            lg_rows = synth.logits(wl, t, rows=rows.tolist())
+            x = fill(t)
+            x[rows_dev] = to_device(lg_rows, dev)
+        else:
+            lg = logits_fn(t)
+            x = to_device(lg, dev)
+            lg_rows = np.ascontiguousarray(lg[rows])
+        bi, tk, sc, dn = gpu.step(x)
         gj, gc = gpu.selection()
         gj, gc = gj.cpu().numpy(), gc.cpu().numpy()
         bi, tk, sc, dn = (x.cpu().numpy() for x in (bi, tk, sc, dn))
-        lg_rows = np.ascontiguousarray(lg[rows])
         oj, oc, on = ref.select(lg_rows)
         for k, b in enumerate(items):
             check_selection((oj[k], oc[k], on[k]),
@@ -131,16 +165,20 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
         assert (dn[sub].astype(bool) == odn).all(), f"{where}: done {dn[sub]} vs {odn}"
         if check_finished:
             compare_finished(gpu, ref, items, where)
+        last = t == steps or dn.all()
         if kv_planes:
+            # position t-1 of every followed row gets distinct words (the other
+            # items' rows are moved by the same launch but not compared)
             for li, (p, hp) in enumerate(zip(planes, host)):
-                blk = np.stack([kv_position(wl, r // W, r % W, t - 1, li, words)
-                                for r in range(wl.rows)])
-                p[:, t - 1] = torch.from_numpy(blk).to(dev)
-                hp[:, t - 1] = blk[rows]
+                blk = np.stack([kv_position(wl, r // W, r % W, t - 1, li, words) for r in rows])
+                p[rows_dev, t - 1] = torch.from_numpy(blk).to(dev)
+                hp[:, t - 1] = blk
             gpu.reorder_kv(planes, t)
             oracle.kv_reorder(host, obi, odn, t)
-            for p, hp in zip(planes, host):
-                assert np.array_equal(p.cpu().numpy()[rows], hp), f"{where}: KV reorder differs"
+            if t % kv_check_every == 0 or last:
+                for li, (p, hp) in enumerate(zip(planes, host)):
+                    assert np.array_equal(p[rows_dev].cpu().numpy(), hp), \
+                        f"{where}: KV reorder differs (plane {li})"
         rep.steps = t
         if dn.all():
             break

@@ -72,8 +72,7 @@ def test_traffic_summaries_are_consistent():
         stem = os.path.basename(p)[:-len("_traffic.json")]
         kernel = next(k for k in bench.TRAFFIC_SOURCES if stem.startswith(k + "_"))
         workload = stem[len(kernel) + 1:]
-        per_search = None if kernel == "k4_verify" else d["steps"]
-        found = bench.measured_traffic(kernel, workload, d["steps"], per_search)
+        found = bench.measured_traffic(kernel, workload, d.get("timed_steps"))
         # a summary taken on an earlier version of the kernel is not reported
         current = d["source_sha256_16"] == bench.kernel_source_hash(kernel)
         assert found == (got if current else None), p
@@ -119,3 +118,38 @@ def test_algorithmic_bytes_by_hand():
     tables = 2 * 2 * (3 * 5 + 2 * 12) * 4
     copies = [2 + 1, 0, 2, 2 + 2]
     assert kvp.tolist() == [2 * c * (t % 2) * per + tables for c, t in zip(copies, ts)]
+
+
+def test_algorithmic_bytes_of_independent_steps():
+    """Timed steps taken from different searches: each step's logit bytes
+    count the rows live after its own search's previous step, given by
+    ``prev``; t = 1 always reads slot 0 of each item."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import bench
+    inf = -np.inf
+    f = 0.0
+    ts = [5, 1, 9]
+    bi = np.array([[[1, 0, 2], [0, 1, 2]],      # item 1 keeps its parents
+                   [[0, 0, 0], [0, 0, 0]],
+                   [[0, 1, 2], [2, 2, 1]]])     # item 0 is done (own slots)
+    sc = np.full((3, 2, 3), f)
+    sc[2, 0] = inf
+    dn = np.array([[0, 0], [0, 0], [1, 0]], bool)
+    # the searches' previous steps: step 4 left item 1 with one dead slot;
+    # step 8 left item 0 done
+    psc = np.array([[[f, f, f], [f, f, inf]],
+                    [[inf, inf, inf], [inf, inf, inf]],   # unused for t = 1
+                    [[f, f, f], [f, f, f]]])
+    pdn = np.array([[0, 0], [1, 1], [1, 0]], bool)
+    kv, lg, rd, wr = bench.algorithmic_bytes(ts, bi, sc, dn, V=10, elem_bytes=4, bpp=16,
+                                             planes=2, prev=(psc, pdn))
+    state = 20 * 2 * 3
+    assert lg.tolist() == [5 * 40 + state, 2 * 40 + state, 3 * 40 + state]
+    per = 16 * 2
+    # t=5: item 0 swaps 0 and 1 (2 writes + 2 reads); t=1: slots 1, 2 of both
+    # items from parent 0; t=9: item 1 moves 0, 1 from 2 and 2 from 1
+    assert kv.tolist() == [4 * 5 * per, 6 * 1 * per, 5 * 9 * per]
+    assert bench.schedule(20, 200) == list(range(6, 200, 10))
+    assert bench.schedule(200, 200) == list(range(1, 201))
+    assert bench.schedule(3, 128) == [22, 65, 107]

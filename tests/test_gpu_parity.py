@@ -129,6 +129,35 @@ def test_llama3_8b_sampled_items(dev):
     g.close()
 
 
+def test_llama3_8b_full_search(dev):
+    """The Llama-shaped search for all 200 steps: items 0 and 5 followed by the
+    oracle (the other items' rows drawn on the GPU keep every launch at B=8),
+    64 KV planes of 2 KiB per position (each XCD streams whole planes;
+    gen_len up to 200) compared every 20 steps, then the final hypotheses."""
+    wl = synth.WORKLOADS["llama3_8b"]
+    items = [0, 5]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=64,
+                               other_rows="device", kv_check_every=20)
+    assert rep.steps == wl.max_steps
+    compare_final(g, ref, items, wl.num_return, "llama3_8b, 200 steps")
+    log(f"llama3_8b full search: {rep}")
+    g.close()
+
+
+def test_wide_beam_twenty_steps(dev):
+    """The wide search (B=16, W=16, V=250000 fp32) for 20 steps: items 3 and
+    12 followed by the oracle, two KV planes of 4 KiB per position compared
+    every 5 steps, then the final hypotheses at step 20."""
+    wl = synth.WORKLOADS["wide"]
+    items = [3, 12]
+    rep, g, ref = run_stepwise(wl, 20, dev, items=items, kv_planes=2, other_rows="device",
+                               kv_check_every=5)
+    assert rep.steps == 20
+    compare_final(g, ref, items, wl.num_return, "wide, 20 steps")
+    log(f"wide 20 steps: {rep}")
+    g.close()
+
+
 def test_llama3_8b_with_reachable_eos(dev):
     """The Llama-shaped workload with EOS = 1 outside the Zipf term and a
     rising EOS bias, so that the EOS path and early stopping run at V=128256."""
@@ -473,6 +502,64 @@ def test_error_paths_on_device(dev):
     g.close()
 
 
+def test_rejected_calls_enqueue_nothing(dev):
+    """BS_EINVAL and BS_ESTATE are decided on the host before any launch: a
+    step with a NULL output leaves the step count and the next step as they
+    were; a reorder over 130 planes (two launches) whose last plane pointer is
+    NULL, or whose plane address is not 4-byte aligned, moves nothing in any
+    plane; a paged reorder with a NULL pool or the wrong gen_len leaves the
+    block table as it was; a step past max_steps is refused."""
+    import beam_search_step_amd as bs
+    L = bs.library()
+    g = bs.BeamSearch(1, 2, 3, 2, lp="none", alpha=0.0)
+    x1 = torch.from_numpy(np.log(np.array([[0.5, 0.4, 0.1]] * 2)).astype(np.float32)).to(dev)
+    rc = L.bs_step(g.h, x1.data_ptr(), 3, None, g.token_id.data_ptr(), g.scores.data_ptr(),
+                   g.done.data_ptr())
+    assert rc == bs.BS_EINVAL and g.steps == 0
+    bi, tk, sc, dn = g.step(x1)   # slots A, B, both from parent 0: slot 1 moves
+    assert bi.tolist() == [[0, 0]] and tk.tolist() == [[0, 1]] and g.steps == 1
+
+    planes = [torch.tensor([[[p, 0, 0, 0]], [[p, 1, 1, 1]]], dtype=torch.int32, device=dev)
+              for p in range(130)]
+    before = [p.clone() for p in planes]
+    desc = bs.make_kv_desc(planes)
+    desc._keep[129] = None
+    assert L.bs_reorder_kv(g.h, ctypes.byref(desc), 1) == bs.BS_EINVAL
+    raw = torch.zeros(2 * 16 + 1, dtype=torch.int32, device=dev)
+    odd = bs.make_kv_desc(planes)
+    odd._keep[0] = raw.data_ptr() + 2          # not a multiple of 4 bytes
+    assert L.bs_reorder_kv(g.h, ctypes.byref(odd), 1) == bs.BS_EINVAL
+    torch.cuda.synchronize()
+    assert all(torch.equal(p, q) for p, q in zip(planes, before)), "a refused reorder moved rows"
+    assert raw.count_nonzero().item() == 0
+    g.reorder_kv(planes, 1)                    # the valid call moves row 0 into row 1
+    for p, q in zip(planes, before):
+        assert torch.equal(p[1], q[0]) and torch.equal(p[0], q[0])
+
+    x2 = torch.from_numpy(np.log(np.array([[0.40, 0.35, 0.25], [0.90, 0.06, 0.04]]))
+                          .astype(np.float32)).to(dev)
+    g.step(x2)
+    rc = L.bs_step(g.h, x2.data_ptr(), 3, g.beam_idx.data_ptr(), g.token_id.data_ptr(),
+                   g.scores.data_ptr(), g.done.data_ptr())
+    assert rc == bs.BS_ESTATE and g.steps == 2   # max_steps = 2 taken
+    g.close()
+
+    # the paged cache: refused reorders leave the table as it was
+    g = bs.BeamSearch(1, 2, 3, 4, lp="none", alpha=0.0)
+    pk = bs.PagedKV(g, 2)
+    pools = [torch.zeros((pk.blocks_per_item, 2, 4), dtype=torch.int32, device=dev)]
+    g.step(x1)
+    table0 = pk.table()
+    desc = bs.make_kv_pool(pools)
+    assert L.bs_kv_paged_reorder(pk.h, ctypes.byref(desc), 2) == bs.BS_ESTATE  # gen_len != t
+    desc._keep[0] = None
+    assert L.bs_kv_paged_reorder(pk.h, ctypes.byref(desc), 1) == bs.BS_EINVAL
+    assert torch.equal(pk.table(), table0)
+    pk.reorder(pools, 1)
+    pk.close()
+    g.close()
+
+
 def test_wrappers_reject_bad_tensors_before_launching(dev):
     """The Python wrappers refuse tensors a kernel would read or write out of
     bounds, before any launch; the handle's state is unchanged."""
@@ -673,6 +760,44 @@ def test_kv_reorder_region_above_the_streaming_threshold(dev):
     oracle.kv_reorder(host, obi, odn, gen)
     for li, (p, h) in enumerate(zip(planes, host)):
         assert np.array_equal(p.cpu().numpy(), h), f"plane {li} differs"
+    g.close()
+
+
+@pytest.mark.parametrize("n_planes,gen", [(12, 100), (16, 80)])
+def test_kv_reorder_w16_above_the_streaming_threshold(dev, n_planes, gen):
+    """The wide shape's reorder once its region passes 1 GiB (the wide search
+    gets there at t ~ 86): 16 items x 16 slots, 4 KiB positions, nontemporal
+    parent reads, up to 15 destination slots per parent (a thread waits for
+    its stores after every fourth), over 12 planes (grid order, as the wide
+    shape's 6 layers x K|V) and 16 planes (each XCD streams whole planes),
+    after each of three steps that move slots; bit for bit against the
+    oracle's gather."""
+    import beam_search_step_amd as bs
+    B, W, V, words = 16, 16, 40, 1024
+    assert B * W * gen * words * 4 * n_planes > 2 ** 30
+    wl = synth.WORKLOADS["toy"].replace(batch=B, beam=W, vocab=V, eos_id=-1, stop="never",
+                                        lp="none", alpha=0.0, max_steps=3, seed=98 + n_planes)
+    g = bs.BeamSearch.for_workload(wl)
+    ref = oracle.Search.for_workload(wl)
+    rng = np.random.default_rng(n_planes)
+    host = [rng.integers(-2 ** 31, 2 ** 31 - 1, size=(B * W, gen, words), dtype=np.int32)
+            for _ in range(n_planes)]
+    planes = [torch.from_numpy(h).to(dev) for h in host]
+    moved = shared = 0
+    for t in (1, 2, 3):
+        lg = synth.logits(wl, t)
+        bi, tk, sc, dn = g.step(to_device(lg, dev))
+        obi, otk, osc, odn = ref.step(lg)
+        assert np.array_equal(bi.cpu().numpy(), obi), f"t={t}: beam_idx differs"
+        for b in range(B):
+            mv = [w for w in range(W) if osc[b, w] > -np.inf and obi[b, w] != w]
+            moved += len(mv)
+            shared += len(mv) - len({int(obi[b, w]) for w in mv})
+        g.reorder_kv(planes, gen)
+        oracle.kv_reorder(host, obi, odn, gen)
+        for li, (p, h) in enumerate(zip(planes, host)):
+            assert np.array_equal(p.cpu().numpy(), h), f"t={t} plane {li} differs"
+    assert moved > 3 * B and shared > 0, (moved, shared)
     g.close()
 
 
