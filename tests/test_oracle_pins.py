@@ -445,25 +445,46 @@ def test_selection_ties_go_to_lower_flat_index(orc):
 
 
 def test_selection_ties_bf16(orc):
-    """bf16 logits tie often; the order must still be (score desc, j asc)."""
-    wl = synth.WORKLOADS["llama3_8b"].replace(batch=2, beam=3, vocab=300, eos_id=-1)
-    o = orc.Search.for_workload(wl, max_steps=3)
-    for t in (1, 2, 3):
-        lg = synth.logits(wl, t)
-        j, c, n = o.select(lg)
-        x = synth.widen("bf16", lg).astype(np.float64)
-        lse, s = o.lse(), o.scores()
-        for b in range(2):
-            rows = []
-            for w in range(3):
-                if s[b, w] == -np.inf:
-                    continue
-                logp = (x[b * 3 + w] - lse[b, w]).astype(np.float32)
-                cand = (np.float32(s[b, w]) + logp).astype(np.float32)
-                rows += [(-float(cv), w * 300 + v) for v, cv in enumerate(cand)]
-            rows.sort()
-            assert j[b, :3].tolist() == [jj for _, jj in rows[:3]]
-        o.step(lg)
+    """bf16 logits tie often (one ulp is 0.0625 between 8 and 16). Expected
+    selections here follow from the order of the values and the tie rule
+    alone, with no log-sum-exp: a value one bf16 ulp higher ranks first,
+    exact ties go to the lower flat index j = w*V + v, and a dead row takes no
+    part whatever it holds. B=1, W=3, V=300."""
+    V, W = 300, 3
+    bits = lambda a: synth.f32_to_bf16_bits(np.asarray(a, np.float32))   # noqa: E731
+    o = orc.Search(1, W, V, 3, lp="none", alpha=0.0, dtype="bf16")
+    x1 = np.zeros((W, V), np.float32)
+    x1[0, [250, 17, 5, 140]] = [9.0625, 9.0, 9.0, 9.0]
+    x1[1:, :] = 20.0                      # rows 1, 2 are dead at step 1
+    assert np.array_equal(synth.widen("bf16", bits(x1)), x1)   # exact in bf16
+    bi, tk, sc, d = o.step(bits(x1))
+    assert tk.tolist() == [[250, 5, 17]] and bi.tolist() == [[0, 0, 0]]
+    assert sc[0, 0] > sc[0, 1] == sc[0, 2]
+    # every row the same: row 0 leads by the ulp of step 1, rows 1 and 2 tie
+    x2 = np.zeros((W, V), np.float32)
+    x2[:, [3, 9]] = 12.0
+    bi, tk, sc, d = o.step(bits(x2))
+    assert bi.tolist() == [[0, 0, 1]] and tk.tolist() == [[3, 9, 3]]
+    assert sc[0, 0] == sc[0, 1] > sc[0, 2]
+
+
+def test_tbase_eos_schedule_finish_median(orc):
+    """The Transformer-base workload's EOS schedule (its start re-tuned so that
+    searches end mid-way, the survey's criterion being a median finish step
+    between 20 and 100): the first 8 items of the search, run by the oracle
+    to the end, finish at steps whose median lies in that range, none at the
+    first steps and none running to the maximum of 128."""
+    wl = synth.WORKLOADS["tbase"].replace(batch=8)
+    o = orc.Search.for_workload(wl)
+    finish = np.zeros(wl.batch, int)
+    for t in range(1, wl.max_steps + 1):
+        _, _, _, d = o.step(synth.logits(wl, t))
+        finish[(finish == 0) & d] = t
+        if d.all():
+            break
+    assert (finish > 0).all(), finish
+    assert 20 <= np.median(finish) <= 100, finish
+    assert finish.min() > 10 and finish.max() < wl.max_steps, finish
 
 
 # ---------------------------------------------------------------------------
