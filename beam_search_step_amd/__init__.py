@@ -99,6 +99,7 @@ def library() -> ctypes.CDLL:
         L.bs_verify_create.argtypes = [i32, i32, i32, i32, P, ctypes.POINTER(P)]
         L.bs_verify.argtypes = [P, P, i64, P, P, P]
         L.bs_verify_ex.argtypes = [P, P, i64, P, i32, i32, P, P, P]
+        L.bs_verify_noalloc.argtypes = [P, P, i32, i32, i32, i32, i64, P, P, P]
         L.bs_verify_destroy.argtypes = [P]
         L.bs_verify_destroy.restype = None
         for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_reorder_kv_timed",
@@ -106,7 +107,7 @@ def library() -> ctypes.CDLL:
                      "bs_last_selection", "bs_get_finished", "bs_steps_taken",
                      "bs_kv_paged_create", "bs_kv_paged_reset", "bs_kv_paged_table",
                      "bs_kv_paged_reorder", "bs_kv_paged_status",
-                     "bs_verify_create", "bs_verify", "bs_verify_ex"):
+                     "bs_verify_create", "bs_verify", "bs_verify_ex", "bs_verify_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -323,6 +324,15 @@ def bs_verify_ex(h: int, logits, proposals, top_k: int, min_block: int, accept_l
                                   top_k, min_block, _ptr(accept_len), _ptr(argmax),
                                   _ptr(prop_rank) if prop_rank is not None else None),
            "bs_verify_ex")
+
+
+def bs_verify_noalloc(logits, dtype: int, batch: int, k: int, vocab: int, proposals, accept_len,
+                      argmax, stream=None) -> None:
+    """The verify call with the library's static workspace (no handle, no
+    allocation); logits [B*k, S] or [B, k, S]."""
+    _check(library().bs_verify_noalloc(_stream(stream), _ptr(logits), dtype, batch, k, vocab,
+                                       _verify_stride(logits), _ptr(proposals),
+                                       _ptr(accept_len), _ptr(argmax)), "bs_verify_noalloc")
 
 
 def bs_verify_destroy(h: int) -> None:

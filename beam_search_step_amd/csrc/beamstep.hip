@@ -47,6 +47,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "beamstep.h"
 
 #pragma clang fp contract(off)
@@ -369,6 +371,62 @@ void launch_k4_tiles(const K4Args& a, int dtype, bool count, bool aligned, dim3 
   }
 }
 
+// The verify call's launches: the row or tile kernel writes one partial
+// (maximum, its first column, and with COUNT the logits that beat the
+// proposal's) per (row, segment or tile) into px/pv/pc, then k4_accept merges
+// them; every partial is written before it is read, so the buffers need no
+// clearing. tiles: the logits' tiles of kThreads * 16 elements per row.
+int verify_segments_for(int rows, int tiles) {
+  return rows >= kRowVerifyMinRows ? verify_segments(rows, tiles) : tiles;
+}
+
+int launch_verify(hipStream_t s, int dtype, int B, int k, int V, int tiles, const void* logits,
+                  int64_t stride, const int32_t* proposals, int top_k, int min_block,
+                  int32_t* accept_len, int32_t* argmax, int32_t* prop_rank, float* px, int* pv,
+                  int* pc) {
+  const int esize = dtype == BS_BF16 ? 2 : 4;
+  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((stride * esize) % 16 == 0);
+  const bool count = top_k > 1 || prop_rank != nullptr;
+  K4Args a;
+  a.logits = logits;
+  a.stride = stride;
+  a.V = V;
+  a.tile = kThreads * 16;
+  a.tiles = tiles;
+  a.k = k;
+  a.B = B;
+  a.px = px;
+  a.pv = pv;
+  a.pc = pc;
+  a.proposals = proposals;
+  a.accept = accept_len;
+  a.argmax = argmax;
+  a.rank = prop_rank;
+  a.top_k = top_k;
+  a.min_block = min_block;
+  const int rows = B * k;
+  if (rows >= kRowVerifyMinRows) {
+    // enough rows to fill the chip: a few segments per row, one tile each
+    a.tiles = verify_segments(rows, tiles);
+    if (dtype == BS_BF16) {
+      if (count) launch_k4_row<uint16_t, true>(a, aligned, rows, s);
+      else launch_k4_row<uint16_t, false>(a, aligned, rows, s);
+    } else {
+      if (count) launch_k4_row<float, true>(a, aligned, rows, s);
+      else launch_k4_row<float, false>(a, aligned, rows, s);
+    }
+  } else {
+    launch_k4_tiles(a, dtype, count, aligned, dim3(tiles, rows), s);
+  }
+  int rc = launch_status();
+  if (rc != BS_OK) return rc;
+  if (count)
+    hipLaunchKernelGGL((k4_accept<true>), dim3(B), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k4_accept<false>), dim3(B), dim3(64), 0, s, a);
+  return launch_status();
+}
+
 int launch_init(bs_state* h) {
   InitArgs ia;
   ia.st = h->st;
@@ -385,6 +443,41 @@ int launch_init(bs_state* h) {
   return launch_status();
 }
 
+}  // namespace
+
+// ---- workspace of bs_verify_noalloc ---------------------------------------
+// For callers that cannot allocate device memory, the verify call's partials
+// live in this array instead of a handle's allocation: each GPU the library
+// runs on holds its own copy until the process ends, and every
+// bs_verify_noalloc call on that GPU uses it (calls that overlap on one GPU
+// race). Host code never passes `scratch` itself to a kernel -- in host code
+// the name is a host-side stand-in -- but the device address that
+// hipGetSymbolAddress gives for the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// the current device's address of `scratch`
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BS_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return BS_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return BS_EDEVICE;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BS_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -935,52 +1028,35 @@ int bs_verify_ex(bs_verify_state* h, const void* logits, int64_t row_stride_elem
   if (!h || !logits || !proposals || !accept_len || !argmax) return BS_EINVAL;
   if (row_stride_elems < h->V || top_k < 1 || min_block < 0 || min_block > h->k)
     return BS_EINVAL;
-  const int esize = h->dtype == BS_BF16 ? 2 : 4;
-  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((row_stride_elems * esize) % 16 == 0);
-  const bool count = top_k > 1 || prop_rank != nullptr;
-  K4Args a;
-  a.logits = logits;
-  a.stride = row_stride_elems;
-  a.V = h->V;
-  a.tile = h->tile;
-  a.tiles = h->tiles;
-  a.k = h->k;
-  a.B = h->B;
-  a.px = h->px;
-  a.pv = h->pv;
-  a.pc = h->pc;
-  a.proposals = proposals;
-  a.accept = accept_len;
-  a.argmax = argmax;
-  a.rank = prop_rank;
-  a.top_k = top_k;
-  a.min_block = min_block;
-  const int rows = h->B * h->k;
-  if (rows >= kRowVerifyMinRows) {
-    // enough rows to fill the chip: a few segments per row, one tile each
-    a.tiles = verify_segments(rows, h->tiles);
-    if (h->dtype == BS_BF16) {
-      if (count) launch_k4_row<uint16_t, true>(a, aligned, rows, h->stream);
-      else launch_k4_row<uint16_t, false>(a, aligned, rows, h->stream);
-    } else {
-      if (count) launch_k4_row<float, true>(a, aligned, rows, h->stream);
-      else launch_k4_row<float, false>(a, aligned, rows, h->stream);
-    }
-  } else {
-    launch_k4_tiles(a, h->dtype, count, aligned, dim3(h->tiles, rows), h->stream);
-  }
-  int rc = launch_status();
-  if (rc != BS_OK) return rc;
-  if (count)
-    hipLaunchKernelGGL((k4_accept<true>), dim3(h->B), dim3(64), 0, h->stream, a);
-  else
-    hipLaunchKernelGGL((k4_accept<false>), dim3(h->B), dim3(64), 0, h->stream, a);
-  return launch_status();
+  return launch_verify(h->stream, h->dtype, h->B, h->k, h->V, h->tiles, logits,
+                       row_stride_elems, proposals, top_k, min_block, accept_len, argmax,
+                       prop_rank, h->px, h->pv, h->pc);
 }
 
 int bs_verify(bs_verify_state* h, const void* logits, int64_t row_stride_elems,
               const int32_t* proposals, int32_t* accept_len, int32_t* argmax) {
   return bs_verify_ex(h, logits, row_stride_elems, proposals, 1, 0, accept_len, argmax, nullptr);
+}
+
+int bs_verify_noalloc(void* hip_stream, const void* logits, int32_t logits_dtype, int32_t batch,
+                      int32_t k, int32_t vocab, int64_t row_stride_elems,
+                      const int32_t* proposals, int32_t* accept_len, int32_t* argmax) {
+  if (!logits || !proposals || !accept_len || !argmax) return BS_EINVAL;
+  if (batch < 1 || k < 1 || k > 64 || vocab < 1 || row_stride_elems < vocab) return BS_EINVAL;
+  if ((int64_t)batch * k > kMaxGridRows) return BS_EINVAL;
+  if (logits_dtype != BS_F32 && logits_dtype != BS_BF16) return BS_EINVAL;
+  const int rows = batch * k;
+  const int tiles = (vocab + kThreads * 16 - 1) / (kThreads * 16);
+  const size_t part = align_up((size_t)rows * verify_segments_for(rows, tiles) * 4);
+  if (2 * part > kScratchBytes) return BS_EINVAL;
+  void* base = nullptr;
+  const int rc = scratch_address(&base);
+  if (rc != BS_OK) return rc;
+  float* px = (float*)base;
+  int* pv = (int*)((char*)base + part);
+  return launch_verify((hipStream_t)hip_stream, logits_dtype, batch, k, vocab, tiles, logits,
+                       row_stride_elems, proposals, 1, 0, accept_len, argmax, nullptr, px, pv,
+                       nullptr);
 }
 
 void bs_verify_destroy(bs_verify_state* h) {

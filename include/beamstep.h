@@ -379,6 +379,28 @@ int bs_verify_ex(bs_verify_state *h, const void *logits, int64_t row_stride_elem
                  const int32_t *proposals, int32_t top_k, int32_t min_block,
                  int32_t *accept_len, int32_t *argmax, int32_t *prop_rank);
 
+/* bs_verify without a handle and without allocating, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc. Computes what bs_verify computes (the
+ * exact criterion) for logits [batch][k][vocab] of logits_dtype, on
+ * hip_stream (NULL: the null stream). Its per-segment partials live in a
+ * static device array of the library, 4 MiB on each GPU, held until the
+ * process ends and shared by every bs_verify_noalloc call on that GPU:
+ * calls that overlap on one GPU (other streams, other threads) race, so
+ * order them on one stream. Nothing in the array needs clearing between
+ * calls. The first call on a device looks up the array's address there
+ * (hipGetSymbolAddress): make it outside graph capture.
+ *   logits, proposals, accept_len, argmax, row_stride_elems: as bs_verify
+ *   Limits: batch >= 1, k in 1..64, batch*k <= 65535 (as bs_verify_create),
+ *   and the partials within the array: batch*k*S <= 524288, S being the
+ *   segments of a row, ceil(vocab / 4096) when batch*k < 256 and at most 4
+ *   otherwise (so every shape with batch*k >= 256 fits).
+ * Errors: BS_EINVAL (NULL pointer, stride < vocab, a shape out of range or
+ * beyond the array); BS_EDEVICE. */
+int bs_verify_noalloc(void *hip_stream, const void *logits, int32_t logits_dtype,
+                      int32_t batch, int32_t k, int32_t vocab, int64_t row_stride_elems,
+                      const int32_t *proposals, int32_t *accept_len, int32_t *argmax);
+
 void bs_verify_destroy(bs_verify_state *h);
 
 /* Static description of a status code. */
