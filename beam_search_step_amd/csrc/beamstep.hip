@@ -239,9 +239,6 @@ constexpr int kK3Words = 1;
 // workgroups along a row: the grid's x extent times the workgroup size must
 // stay below 2^32 work-items
 constexpr int64_t kK3MaxTiles = 0xFFFFFFFFll / kK3Threads;
-// a launch whose region (rows x gen_len positions x planes) exceeds this reads
-// its parents with the nontemporal hint: four times the 256 MB Infinity Cache
-constexpr int64_t kK3StreamBytes = (int64_t)1 << 30;
 
 // Timing events (either may be null) are attached to the dispatch itself
 // (hipExtLaunchKernel), so they take the kernel's own start and end and put
@@ -255,14 +252,11 @@ void launch_k3_c(const K3Args& a, int B, int nplanes, hipStream_t s, LaunchEvent
   constexpr int NP = kK3Words;
   const int64_t tiles = (a.words + (int64_t)kK3Threads * NP - 1) / ((int64_t)kK3Threads * NP);
   dim3 g((unsigned)tiles, B, nplanes);
-  K3Args b = a;
-  b.whole_planes = nplanes % 8 == 0 && tiles * B * nplanes < 0xFFFFFFFFll;
-  b.stream_loads = a.region_bytes_per_plane * nplanes > kK3StreamBytes;
   if (ev.start || ev.stop)
     hipExtLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s,
-                          ev.start, ev.stop, 0, b);
+                          ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, b);
+    hipLaunchKernelGGL((k3_kv_reorder<WMAX, WORD, NP, CONTIG>), g, dim3(kK3Threads), 0, s, a);
 }
 template <int WMAX>
 void launch_k3_w(const K3Args& a, int word, bool contig, int B, int nplanes, hipStream_t s,
@@ -729,7 +723,6 @@ static int reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len, Launch
   a.base_off = base_off;
   a.words_per_pos = kv->bytes_per_pos / word;
   a.words = (int64_t)gen_len * a.words_per_pos;
-  a.region_bytes_per_plane = (int64_t)h->rows * gen_len * kv->bytes_per_pos;
   if ((a.words + kK3Threads * kK3Words - 1) / (kK3Threads * kK3Words) > kK3MaxTiles)
     return BS_EINVAL;
   a.W = h->W;

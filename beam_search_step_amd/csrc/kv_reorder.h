@@ -18,9 +18,6 @@ struct K3Args {
   int64_t words_per_pos;
   int W;
   const int* plan;
-  int whole_planes;     // 1: XCD i takes the i-th eighth of the planes
-  int stream_loads;     // 1: parent words are read with the nontemporal hint
-  int64_t region_bytes_per_plane;  // rows x gen_len x bytes_per_pos (host side)
 };
 
 template <int WORD>
@@ -42,30 +39,18 @@ template <int WMAX, typename WT, int NP, bool FULL>
 __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row_stride,
                                            const int64_t (&off)[NP], int64_t e0, int64_t words,
                                            int nsrc, const int (&src)[WMAX],
-                                           const int (&dmask)[WMAX], bool stream_loads) {
+                                           const int (&dmask)[WMAX]) {
   bool ok[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) ok[k] = FULL || e0 + (int64_t)k * kK3Threads < words;
   WT v[NP][WMAX];
-  if (stream_loads) {  // uniform: one loop each way, so no load waits on a branch
 #pragma unroll
-    for (int q = 0; q < WMAX; ++q) {
-      if (q < nsrc) {
-        const char* from = base + (row0 + src[q]) * row_stride;
+  for (int q = 0; q < WMAX; ++q) {
+    if (q < nsrc) {
+      const char* from = base + (row0 + src[q]) * row_stride;
 #pragma unroll
-        for (int k = 0; k < NP; ++k)
-          if (ok[k]) v[k][q] = __builtin_nontemporal_load(reinterpret_cast<const WT*>(from + off[k]));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < WMAX; ++q) {
-      if (q < nsrc) {
-        const char* from = base + (row0 + src[q]) * row_stride;
-#pragma unroll
-        for (int k = 0; k < NP; ++k)
-          if (ok[k]) v[k][q] = *reinterpret_cast<const WT*>(from + off[k]);
-      }
+      for (int k = 0; k < NP; ++k)
+        if (ok[k]) v[k][q] = __builtin_nontemporal_load(reinterpret_cast<const WT*>(from + off[k]));
     }
   }
   // In place: a destination row may be another copy's parent. No other thread
@@ -75,10 +60,11 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
   // no-wait maxima).
   __builtin_amdgcn_s_waitcnt(0x0F70);
   // Between destination slots a thread waits for its stores: after every slot
-  // for W <= 4 (measured faster than keeping them all in flight), after every
-  // fourth for wider beams, whose many destinations otherwise serialise on
-  // the store round trip (measured 2% faster at W = 16, 2% slower at W = 4).
-  // Only the wait above, before the first store, matters for correctness.
+  // for W <= 4, after every fourth for wider beams, whose many destinations
+  // otherwise serialise on the store round trip (measured 2% faster at W = 16
+  // with a warm cache). On a cold cache at W = 4, waiting after every slot,
+  // every second slot or never measured within 1% of each other. Only the
+  // wait above, before the first store, matters for correctness.
   constexpr int kSlotsPerWait = WMAX >= 8 ? 4 : 1;
   int nst = 0;
 #pragma unroll
@@ -95,40 +81,25 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
   }
 }
 
-// Parent reads. Plain loads let a launch reuse what the previous step's
-// launch left in the 256 MB Infinity Cache (the rows it wrote are often this
-// step's parents): at the Llama-3-8B shape, t = 50..100, they ran at 6.7-7.5
-// TB/s against 5.3-5.6 with the nontemporal hint. When the launch's region
-// (rows x positions x planes) is several times the cache nothing survives to
-// the next launch, and reads that do not allocate leave the launch's own
-// lines in place: 4.5-7% faster per launch at the wide shape, t >= 128. The
-// host sets stream_loads when that region exceeds 1 GiB.
+// Parent reads and moved-slot writes both carry the nontemporal hint: every
+// word is read once and written once per launch, and in a decoder the model's
+// forward pass (weights and the whole KV cache) runs between two reorders, so
+// nothing a launch leaves in the 256 MB Infinity Cache is there for the next.
+// Measured with every step's reorder on a cold cache (the Llama-3-8B shape,
+// 20 steps spread over the 200-step search): nontemporal parent reads 5.93
+// TB/s against 5.35 with plain ones; plain stores 5.11.
 //
-// Work order. The hardware hands consecutive workgroups (x fastest, then y,
-// z) to the 8 XCDs in turn, so in grid order every XCD takes every eighth
-// tile of every row span. With whole_planes set (the launch's plane count a
-// multiple of 8, its workgroups fewer than 2^32), the workgroup that XCD i
-// receives k-th does the k-th workgroup of the i-th eighth of the grid
-// instead: XCD i streams planes [i*planes/8, (i+1)*planes/8) from end to end,
-// all items of each, and every XCD still gets the same share of every item.
-// Measured 1.3% faster than grid order with 64 planes of 8 items; an eighth
-// that does not end on a plane boundary lets some XCDs take most of the
-// heavy or unfinished items, and was slower (12 planes: 1.5% with 16 items,
-// 9% when many items had finished).
+// Work order: grid order. The hardware hands consecutive workgroups (x
+// fastest, then y, z) to the 8 XCDs in turn, so every XCD streams every eighth
+// tile of every row span, and every item's share is spread over all XCDs.
+// Giving each XCD whole planes instead (workgroup k of XCD i doing the k-th of
+// the i-th eighth of the grid) measured 1.3% faster when the previous step's
+// rows were still in the cache, but slower on a cold cache (5.79 against 5.93
+// TB/s).
 template <int WMAX, int WORD, int NP, bool CONTIG>
 __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
   using WT = typename Word<WORD>::type;
-  uint32_t bx = blockIdx.x, b = blockIdx.y, bz = blockIdx.z;
-  if (a.whole_planes) {
-    const uint32_t gx = gridDim.x, gy = gridDim.y;
-    const uint32_t lin = bx + gx * (b + gy * bz);
-    const uint32_t eighth = (gx * gy * gridDim.z) >> 3;
-    const uint32_t l2 = (lin & 7) * eighth + (lin >> 3);
-    const uint32_t pl = l2 / gx;
-    bx = l2 - pl * gx;
-    bz = pl / gy;
-    b = pl - bz * gy;
-  }
+  const uint32_t bx = blockIdx.x, b = blockIdx.y, bz = blockIdx.z;
   const int* plan = a.plan + b * kPlanStride;
   // the whole plan is read up front, in one batch of scalar loads: a plan read
   // after a store would be a vector load whose wait also waits for every
@@ -159,11 +130,10 @@ __global__ __launch_bounds__(kK3Threads) void k3_kv_reorder(K3Args a) {
   // every word of the tile is in range (uniform), except in the last tile
   const int64_t e0 = (int64_t)bx * NP * kK3Threads + threadIdx.x;
   if ((int64_t)(bx + 1) * NP * kK3Threads <= a.words)
-    move_words<WMAX, WT, NP, true>(base, row0, a.row_stride, off, e0, a.words, nsrc, src, dmask,
-                                   a.stream_loads);
+    move_words<WMAX, WT, NP, true>(base, row0, a.row_stride, off, e0, a.words, nsrc, src, dmask);
   else
     move_words<WMAX, WT, NP, false>(base, row0, a.row_stride, off, e0, a.words, nsrc, src,
-                                    dmask, a.stream_loads);
+                                    dmask);
 }
 
 }  // namespace

@@ -132,8 +132,8 @@ def test_llama3_8b_sampled_items(dev):
 def test_llama3_8b_full_search(dev):
     """The Llama-shaped search for all 200 steps: items 0 and 5 followed by the
     oracle (the other items' rows drawn on the GPU keep every launch at B=8),
-    64 KV planes of 2 KiB per position (each XCD streams whole planes;
-    gen_len up to 200) compared every 20 steps, then the final hypotheses."""
+    64 KV planes of 2 KiB per position (gen_len up to 200) compared every 20
+    steps, then the final hypotheses."""
     wl = synth.WORKLOADS["llama3_8b"]
     items = [0, 5]
     rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=64,
@@ -732,11 +732,11 @@ def _kv_layout_case(dev, layout, W, timed):
     g.close()
 
 
-def test_kv_reorder_region_above_the_streaming_threshold(dev):
-    """A reorder whose region (rows x positions x planes) exceeds 1 GiB reads
-    its parents with the nontemporal hint: 16 rows x 1025 positions x 8 KiB x
-    8 planes = 1.07 GB, after a step that moves slots, against the oracle's
-    gather, bit for bit."""
+def test_kv_reorder_region_above_a_gib(dev):
+    """A reorder whose region (rows x positions x planes) exceeds 1 GiB, four
+    times the Infinity Cache: 16 rows x 1025 positions x 8 KiB x 8 planes =
+    1.07 GB, after a step that moves slots, against the oracle's gather, bit
+    for bit (row spans of 2^19 words: offsets past 2^31 bytes)."""
     import beam_search_step_amd as bs
     B, W, V = 4, 4, 40
     wl = synth.WORKLOADS["toy"].replace(batch=B, beam=W, vocab=V, eos_id=-1, stop="never",
@@ -764,12 +764,11 @@ def test_kv_reorder_region_above_the_streaming_threshold(dev):
 
 
 @pytest.mark.parametrize("n_planes,gen", [(12, 100), (16, 80)])
-def test_kv_reorder_w16_above_the_streaming_threshold(dev, n_planes, gen):
+def test_kv_reorder_w16_above_a_gib(dev, n_planes, gen):
     """The wide shape's reorder once its region passes 1 GiB (the wide search
-    gets there at t ~ 86): 16 items x 16 slots, 4 KiB positions, nontemporal
-    parent reads, up to 15 destination slots per parent (a thread waits for
-    its stores after every fourth), over 12 planes (grid order, as the wide
-    shape's 6 layers x K|V) and 16 planes (each XCD streams whole planes),
+    gets there at t ~ 86): 16 items x 16 slots, 4 KiB positions, up to 15
+    destination slots per parent (a thread waits for its stores after every
+    fourth), over 12 planes (the wide shape's 6 layers x K|V) and 16 planes,
     after each of three steps that move slots; bit for bit against the
     oracle's gather."""
     import beam_search_step_amd as bs
