@@ -19,8 +19,8 @@ and the i-th timed step is t_i = floor((2i+1) T / 2K) + 1, the middle of the
 i-th (t = 6, 16, ..., 196 for K = 20, T = 200; every step once for K = T).
 Each timed step runs on a search of its own (a handle with its own KV
 cache), brought to step t_i - 1 before the timed region by running steps 1 ..
-t_i - 1; so the timed region is K real decode steps issued back to back,
-whose mix is that of the whole search. No timed step finds in the caches
+t_i - 1; so the timed region is K real decode steps issued back to back
+(longest first), whose mix is that of the whole search. No timed step finds in the caches
 what the previous timed step wrote (each search's KV cache is its own
 memory), as in a decoder whose model forward runs between two steps.
 
@@ -111,6 +111,9 @@ def parse(argv=None):
                          "an event pair recorded around every reorder call")
     ap.add_argument("--copy-reference", type=int, default=1,
                     help="time a plain 1 GiB device copy after the timed region")
+    ap.add_argument("--log", default="",
+                    help="also write a JSONL log: one record per timed step (t, bytes, the "
+                         "events pass's durations), then the bench line")
     return ap.parse_args(argv)
 
 
@@ -174,6 +177,12 @@ def main(argv=None):
         out = bench_search(args, torch, bs, dev, region)
     if args.copy_reference:
         out["copy_reference"] = copy_reference(torch, dev, region)
+    per_step = out.pop("_per_step", [])
+    if args.log:
+        with open(args.log, "w") as f:
+            for rec in per_step:
+                f.write(json.dumps(rec) + "\n")
+            f.write(json.dumps(out) + "\n")
     print(json.dumps(out))
 
 
@@ -189,7 +198,6 @@ def bench_search(args, torch, bs, dev, region):
     if wl.name == "llama3_8b":
         assert W * V == 513024 and wl.kv_bytes_per_token == 131072
     K = args.steps
-    ts = schedule(K, T)
     pool_n, distinct_n = POOLS[wl.name]
     # at any batch, enough buffers for twice the 256 MB Infinity Cache
     pool_n = max(pool_n, -(-512_000_000 // (wl.rows * V * wl.elem_bytes)))
@@ -209,9 +217,29 @@ def bench_search(args, torch, bs, dev, region):
 
     stream = torch.cuda.current_stream()
     kw = dict(prune=args.prune, tile_elems=args.tile_elems, select=args.select)
-    # one search per timed step, and one for the warmup
-    searches = [bs.BeamSearch.for_workload(wl, **kw) for _ in range(K)]
+    L = bs.library()
+    pool_ptrs = [pool[i].data_ptr() for i in range(pool_n)]
+    row_stride = pool.stride(1)
+
+    # one whole search first (untimed, selection only): the step at which each
+    # item finishes, and the search's length -- the step after which every item
+    # is done, or T. The timed steps are spread over that length: a step after
+    # it would find every item done and do nothing.
     warm = bs.BeamSearch.for_workload(wl, **kw)
+    dn_all = torch.zeros((T, B), dtype=torch.uint8, device=dev)
+    for t in range(1, T + 1):
+        rc = L.bs_step(warm.h, pool_ptrs[(t - 1) % pool_n], row_stride, warm.beam_idx.data_ptr(),
+                       warm.token_id.data_ptr(), warm.scores.data_ptr(), dn_all[t - 1].data_ptr())
+        if rc:
+            raise bs.BeamStepError(rc, "bs_step")
+    dn_all = dn_all.cpu().numpy().astype(bool)
+    finish = np.where(dn_all.any(0), dn_all.argmax(0) + 1, T)
+    T_run = int(finish.max())
+    ts = schedule(K, T_run)
+    warm.reset()
+
+    # one search per timed step
+    searches = [bs.BeamSearch.for_workload(wl, **kw) for _ in range(K)]
     paged = args.kv == "paged"
     bsz = args.block_size
     words = bpp // 4
@@ -235,9 +263,10 @@ def bench_search(args, torch, bs, dev, region):
                       for t in ts]
             region_of = list(range(K))
         else:
-            n_reg = int(max(2, min(K, KV_BUDGET_BYTES // (T * per_pos))))
-            kv_mem = [torch.zeros((planes_n, wl.rows, T, words), dtype=torch.int32, device=dev)
-                      for _ in range(n_reg)]
+            t_max = max(ts)
+            n_reg = int(max(2, min(K, KV_BUDGET_BYTES // (t_max * per_pos))))
+            kv_mem = [torch.zeros((planes_n, wl.rows, t_max, words), dtype=torch.int32,
+                                  device=dev) for _ in range(n_reg)]
             region_of = [i % n_reg for i in range(K)]
         # the warmup search: its own region of min(warmup, T) positions
         kv_mem.append(torch.zeros((planes_n, wl.rows, max(1, min(args.warmup, T)), words),
@@ -271,9 +300,6 @@ def bench_search(args, torch, bs, dev, region):
     # beforehand, so that the host issues a step in a few microseconds: the
     # early steps of a search take the GPU less time than the Python wrappers
     # would take to issue them
-    L = bs.library()
-    pool_ptrs = [pool[i].data_ptr() for i in range(pool_n)]
-    row_stride = pool.stride(1)
     desc_refs = [ctypes.byref(d) for d in descs]
     step_c = L.bs_step
     kv_c = L.bs_kv_paged_reorder if paged else L.bs_reorder_kv
@@ -306,9 +332,16 @@ def bench_search(args, torch, bs, dev, region):
             if paged:
                 reorder(i, t)
 
+    # the timed steps belong to independent searches, so their order does not
+    # change the work; the longest go first, so that the host issues the short
+    # ones while the GPU is busy with the long ones instead of the GPU waiting
+    # for the host at the start
+    order = sorted(range(K), key=lambda i: -ts[i])
+
     def run(with_events):
         """The K timed steps, issued back to back."""
-        for i, t in enumerate(ts):
+        for i in order:
+            t = ts[i]
             call(step_c(searches[i].h, pool_ptrs[(t - 1) % pool_n], row_stride, *hist_ptrs[i]),
                  "bs_step")
             if with_events == 2:
@@ -384,14 +417,15 @@ def bench_search(args, torch, bs, dev, region):
         "config": {
             "workload": f"{wl.name}_beam_step: B={B} W={W} V={V} {wl.dtype} logits, KV "
                         f"{wl.layers}x{wl.kv_heads}x{wl.head_dim} {wl.kv_dtype}, {T} steps/search, "
-                        f"gen_len = t; the {K} timed steps are one per stratum of the {T}-step "
-                        f"search ({where}), each on a search of its own brought to step t-1 "
-                        f"outside the timed region"
+                        f"gen_len = t; the {K} timed steps are one per stratum of the {T_run} steps "
+                        f"the search runs ({where}), each on a search of its own brought to step "
+                        f"t-1 outside the timed region"
                         + (", 2W-candidate fill" if args.prune == "top2w" else "")
                         + (", two-pass selection" if args.select == "two_pass" else "")
                         + (f", paged KV (blocks of {bsz} positions, copy on write)" if paged else ""),
             "batch": B, "beam": W, "vocab": V, "logits_dtype": wl.dtype, "prune": args.prune,
-            "kv_bytes_per_token": wl.kv_bytes_per_token, "steps_per_search": T,
+            "kv_bytes_per_token": wl.kv_bytes_per_token, "max_steps": T,
+            "steps_per_search": T_run,
             "timed_steps": ts, "logit_pool_buffers": pool_n, "kv": args.kv,
             "select": args.select, **({"block_size": bsz} if paged else {}),
         },
@@ -403,16 +437,16 @@ def bench_search(args, torch, bs, dev, region):
     out["alg_frac_whole_step"] = out["alg_gbs_whole_step"] / PEAK_HBM_GBS
     if ev_mode:
         d_kv = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3
-        # between one step's reorder and the next: the next step's bs_step
-        d_step = np.array([events[i - 1][1].elapsed_time(events[i][0])
-                           for i in range(1, len(events))]) * 1e-3
+        # between one step's reorder and the next issued: the next step's bs_step
+        d_step = np.array([events[order[j - 1]][1].elapsed_time(events[order[j]][0])
+                           for j in range(1, K)]) * 1e-3
         ach = kv_bytes.sum() / d_kv.sum() / 1e9
-        step_gbs = logit_bytes[1:].sum() / d_step.sum() / 1e9 if K > 1 else None
+        step_gbs = logit_bytes[order[1:]].sum() / d_step.sum() / 1e9 if K > 1 else None
         # the reorder at a few points of the search: the timed steps nearest
         # to t = 1, T/4, T/2, 3T/4 and T
         tsa = np.array(ts)
         curve = {}
-        for tq in (1, T // 4, T // 2, 3 * T // 4, T):
+        for tq in (1, T_run // 4, T_run // 2, 3 * T_run // 4, T_run):
             i = int(np.argmin(np.abs(tsa - tq)))
             if d_kv[i] > 0:
                 curve[str(ts[i])] = {"us": 1e6 * d_kv[i], "GBs": kv_bytes[i] / d_kv[i] / 1e9}
@@ -455,6 +489,20 @@ def bench_search(args, torch, bs, dev, region):
                                 else "event records around each reorder call")
         # the events pass: the same steps, slower by the events' stalls
         out["events_pass_ms_per_step"] = 1e3 * elapsed_ev / K
+    out["finish_steps"] = {"median": float(np.median(finish)), "min": int(finish.min()),
+                           "max": int(finish.max()),
+                           "items_done_before_the_last_step": int((finish < T).sum())}
+    per_step = []
+    for i, t in enumerate(ts):
+        rec = {"t": t, "kv_bytes": float(kv_bytes[i]), "logit_bytes": float(logit_bytes[i]),
+               "live_items_after": int((~dn[i].astype(bool)).sum())}
+        if ev_mode:
+            rec["reorder_us"] = 1e6 * float(d_kv[i])
+            j = order.index(i)
+            if j:
+                rec["step_kernels_us"] = 1e6 * float(d_step[j - 1])
+        per_step.append(rec)
+    out["_per_step"] = per_step
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, bpp, planes_n, args.prune)
     out["input_generation_s"] = gen_s
