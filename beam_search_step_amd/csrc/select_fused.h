@@ -70,19 +70,17 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   const int vend = min(a.V, v0 + a.tile);
   const int K = a.K;  // candidates kept per tile
 
-  // The row's state and the tile are requested together, and the test waits
-  // for both: a dead row or a finished item costs its (wasted) tile loads, but
-  // a live row's logits are not held back by the state's round trip. An empty
-  // asm with a memory clobber keeps the compiler from sinking the state loads
-  // below the tile's waits. The flag byte is read through its aligned 32-bit
-  // word, a scalar load (the flags array is 256-byte aligned and padded to a
-  // multiple of 256 bytes).
+  // The row's state first: a dead row or a finished item loads nothing. The
+  // flag byte is read through its aligned 32-bit word, a scalar load (the
+  // flags array is 256-byte aligned and padded to a multiple of 256 bytes).
+  // Requesting the tile together with the state instead, so that a live row
+  // never waits for the state's round trip, measured no faster (Llama-3-8B
+  // and Transformer-base shapes) and read every finished row's logits.
   const uint32_t done_word = reinterpret_cast<const uint32_t*>(a.done)[b >> 2];
   const float sr = a.s[r];
-  __asm__ volatile("" ::: "memory");
+  if (((done_word >> (8 * (b & 3))) & 0xff) != 0 || sr == -kInf) return;  // nothing to expand
   float x[EPT];
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
-  if (((done_word >> (8 * (b & 3))) & 0xff) != 0 || sr == -kInf) return;  // nothing to expand
 
   // expand, per wave: the wave maximum mw and sum of exp(x - mw); the 16-lane
   // row maxima double as the group maxima for tau

@@ -26,7 +26,8 @@ struct CFArgs {
   int cap;
 };
 
-// The row state and the tile, requested together (as in K1).
+// The row state, then (for a live row of an item still running) the tile, as
+// in K1: a dead row or a finished item loads nothing.
 template <typename T, int EPT, bool ALIGNED>
 __device__ __forceinline__ bool cf_load(const CFArgs& a, int r, int v0, int vend,
                                         float (&x)[EPT], float& sr) {
@@ -34,9 +35,9 @@ __device__ __forceinline__ bool cf_load(const CFArgs& a, int r, int v0, int vend
   const T* row = reinterpret_cast<const T*>(a.logits) + (int64_t)r * a.stride;
   const uint32_t done_word = reinterpret_cast<const uint32_t*>(a.done)[b >> 2];
   sr = a.s[r];
-  __asm__ volatile("" ::: "memory");
+  if (((done_word >> (8 * (b & 3))) & 0xff) != 0 || !(sr > -kInf)) return false;
   load_tile<T, EPT, ALIGNED>(row, v0, vend, x);
-  return ((done_word >> (8 * (b & 3))) & 0xff) == 0 && sr > -kInf;
+  return true;
 }
 
 // L1, grid (tiles, rows): the tile's (max, sum exp) and the maxima of its KP

@@ -148,11 +148,9 @@ int bs_reset(bs_state *h);
  *            with |y| = t; every other selection becomes the next live slot.
  *            Live slots are compacted in rank order; remaining slots are dead
  *            (score -inf). Then the stop rule runs (see bs_stop).
- * Rows of items that are done, and dead rows (score -inf), take no part in
- * the step, whatever they hold (NaN included); their tiles are still loaded,
- * because a tile's loads are issued together with its row's state so that a
- * live row never waits for that state. Every row of the buffer must
- * therefore be readable device memory.
+ * Rows of items that are done, and dead rows (score -inf), are not read:
+ * their logits may hold anything, and need not be valid memory. At step 1
+ * only slot 0 of each item is live, so only rows b*W are read.
  *   logits           device, [B*W][row_stride_elems] of fp32 or bf16 (as
  *                    configured); row r = b*W + w; only the first V of each
  *                    row are read

@@ -447,6 +447,44 @@ def test_massive_ties_and_minus_inf_rows(dev):
     g.close()
 
 
+def test_rows_that_take_no_part_may_hold_nan(dev):
+    """Dead rows (every row but slot 0 at step 1, slots left dead by EOS
+    selections) and the rows of finished items take no part in a step: the
+    same search with NaN in all of them gives the same outputs, selections and
+    finished sets, bit for bit, with the fused and the two-pass selection."""
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["toy"].replace(batch=4, beam=3, vocab=50, eos_id=3, eos_in_zipf=False,
+                                        eos_ramp=2.0, ramp_steps=6, max_steps=8, seed=12,
+                                        num_return=2, stop="true")
+    for select in ("fused", "two_pass"):
+        runs = []
+        for poison in (False, True):
+            g = bs.BeamSearch.for_workload(wl, select=select)
+            scores = np.array([[0.0] + [-np.inf] * (wl.beam - 1)] * wl.batch, np.float32)
+            done = np.zeros(wl.batch, bool)
+            outs = []
+            for t in range(1, wl.max_steps + 1):
+                lg = synth.logits(wl, t).reshape(wl.batch, wl.beam, wl.vocab).copy()
+                if poison:
+                    lg[~np.isfinite(scores) | done[:, None]] = np.nan
+                bi, tk, sc, dn = g.step(torch.from_numpy(lg.reshape(wl.rows, wl.vocab)).to(dev))
+                j, c = g.selection()
+                step = [x.cpu().numpy().copy() for x in (bi, tk, sc, dn, j, c)]
+                outs.append(step)
+                scores, done = step[2], step[3].astype(bool)
+                if done.all():
+                    break
+            outs.append([x.cpu().numpy() for x in g.finalize()])
+            runs.append(outs)
+            g.close()
+        assert len(runs[0]) == len(runs[1])
+        assert any(np.isneginf(o[2]).any() for o in runs[0][:-1]), "no dead slot arose"
+        assert any(o[3].any() for o in runs[0][:-2]), "no item finished before the end"
+        for a, b in zip(*runs):
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y, equal_nan=True), select
+
+
 def test_all_eos_step_and_calls_after_done(dev):
     import beam_search_step_amd as bs
     B, W, V, eos = 2, 3, 50, 7
