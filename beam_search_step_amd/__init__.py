@@ -87,6 +87,9 @@ def library() -> ctypes.CDLL:
         L.bs_last_selection.argtypes = [P, P, P]
         L.bs_get_finished.argtypes = [P, P, P, P, P, P, P]
         L.bs_steps_taken.argtypes = [P]
+        L.bs_state_size.argtypes = [P, ctypes.POINTER(i64)]
+        L.bs_state_save.argtypes = [P, P, i64]
+        L.bs_state_load.argtypes = [P, P, i64]
         L.bs_destroy.argtypes = [P]
         L.bs_destroy.restype = None
         L.bs_kv_paged_create.argtypes = [P, i32, i32, ctypes.POINTER(P)]
@@ -105,6 +108,7 @@ def library() -> ctypes.CDLL:
         for name in ("bs_create", "bs_reset", "bs_step", "bs_reorder_kv", "bs_reorder_kv_timed",
                      "bs_finalize",
                      "bs_last_selection", "bs_get_finished", "bs_steps_taken",
+                     "bs_state_size", "bs_state_save", "bs_state_load",
                      "bs_kv_paged_create", "bs_kv_paged_reset", "bs_kv_paged_table",
                      "bs_kv_paged_reorder", "bs_kv_paged_status",
                      "bs_verify_create", "bs_verify", "bs_verify_ex", "bs_verify_noalloc"):
@@ -297,6 +301,25 @@ def bs_steps_taken(h: int) -> int:
     return library().bs_steps_taken(h)
 
 
+def bs_state_size(h: int) -> int:
+    n = ctypes.c_int64()
+    _check(library().bs_state_size(h, ctypes.byref(n)), "bs_state_size")
+    return n.value
+
+
+def bs_state_save(h: int) -> bytes:
+    """The handle's search state as a snapshot (host bytes); synchronises."""
+    n = bs_state_size(h)
+    buf = ctypes.create_string_buffer(n)
+    _check(library().bs_state_save(h, buf, n), "bs_state_save")
+    return buf.raw
+
+
+def bs_state_load(h: int, snapshot: bytes) -> None:
+    buf = ctypes.create_string_buffer(snapshot, len(snapshot))
+    _check(library().bs_state_load(h, buf, len(snapshot)), "bs_state_load")
+
+
 def bs_destroy(h: int) -> None:
     library().bs_destroy(h)
 
@@ -392,6 +415,13 @@ class BeamSearch:
 
     def reset(self):
         bs_reset(self.h)
+
+    def save(self) -> bytes:
+        """A snapshot of the search (host bytes), to resume it with load()."""
+        return bs_state_save(self.h)
+
+    def load(self, snapshot: bytes) -> None:
+        bs_state_load(self.h, snapshot)
 
     @property
     def steps(self) -> int:

@@ -971,6 +971,83 @@ int bs_get_finished(bs_state* h, float* norm, float* raw, int32_t* len, int32_t*
 
 int bs_steps_taken(const bs_state* h) { return h ? h->t : BS_EINVAL; }
 
+// ---- checkpoint / resume ----------------------------------------------------
+// A snapshot is a header (the configuration it belongs to and the steps taken)
+// followed by the handle's search state, which bs_create laid out as one
+// contiguous range at the start of its allocation: running scores, slot ranks,
+// done flags, finished sets, backpointers, the last selection and the reorder
+// plan (values only, no addresses). What follows that range (the length-penalty
+// table, the per-tile partials) is derived from the configuration or rewritten
+// by every step.
+namespace {
+constexpr uint32_t kSnapMagic = 0x42535331u;  // "BSS1"
+struct SnapHeader {
+  uint32_t magic, header_bytes;
+  int32_t batch, beam, vocab, max_steps, eos_id, pad_id, logits_dtype, lp, stop, num_return;
+  int32_t prune, select, steps_taken, reserved;
+  double alpha;
+  uint64_t state_bytes;
+};
+size_t state_bytes(const bs_state* h) { return (size_t)((const char*)h->lpt - (const char*)h->block); }
+SnapHeader snap_header(const bs_state* h) {
+  SnapHeader x;
+  memset(&x, 0, sizeof(x));
+  x.magic = kSnapMagic;
+  x.header_bytes = sizeof(SnapHeader);
+  x.batch = h->cfg.batch;
+  x.beam = h->cfg.beam;
+  x.vocab = h->cfg.vocab;
+  x.max_steps = h->cfg.max_steps;
+  x.eos_id = h->cfg.eos_id;
+  x.pad_id = h->cfg.pad_id;
+  x.logits_dtype = h->cfg.logits_dtype;
+  x.lp = h->cfg.lp;
+  x.stop = h->cfg.stop;
+  x.num_return = h->cfg.num_return;
+  x.prune = h->cfg.prune;
+  x.select = h->cfg.select;
+  x.steps_taken = h->t;
+  x.alpha = h->cfg.alpha;
+  x.state_bytes = state_bytes(h);
+  return x;
+}
+}  // namespace
+
+int bs_state_size(const bs_state* h, int64_t* bytes) {
+  if (!h || !bytes) return BS_EINVAL;
+  *bytes = (int64_t)(sizeof(SnapHeader) + state_bytes(h));
+  return BS_OK;
+}
+
+int bs_state_save(bs_state* h, void* dst, int64_t capacity) {
+  if (!h || !dst) return BS_EINVAL;
+  const size_t n = state_bytes(h);
+  if (capacity < (int64_t)(sizeof(SnapHeader) + n)) return BS_EINVAL;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) return BS_EDEVICE;
+  const SnapHeader x = snap_header(h);
+  if (hipMemcpy((char*)dst + sizeof(SnapHeader), h->block, n, hipMemcpyDeviceToHost) != hipSuccess)
+    return BS_EDEVICE;
+  memcpy(dst, &x, sizeof(x));
+  return BS_OK;
+}
+
+int bs_state_load(bs_state* h, const void* src, int64_t size) {
+  if (!h || !src || size < (int64_t)sizeof(SnapHeader)) return BS_EINVAL;
+  SnapHeader x, want = snap_header(h);
+  memcpy(&x, src, sizeof(x));
+  // everything but the step count must be this handle's
+  want.steps_taken = x.steps_taken;
+  if (memcmp(&x, &want, sizeof(x)) != 0) return BS_EINVAL;
+  if (x.steps_taken < 0 || x.steps_taken > h->T) return BS_EINVAL;
+  if (size < (int64_t)(sizeof(SnapHeader) + x.state_bytes)) return BS_EINVAL;
+  if (hipMemcpyAsync(h->block, (const char*)src + sizeof(SnapHeader), x.state_bytes,
+                     hipMemcpyHostToDevice, h->stream) != hipSuccess ||
+      hipStreamSynchronize(h->stream) != hipSuccess)
+    return BS_EDEVICE;
+  h->t = x.steps_taken;
+  return BS_OK;
+}
+
 void bs_destroy(bs_state* h) {
   if (!h) return;
   for (bs_kv_paged* p = h->caches; p; p = p->next) p->h = nullptr;  // orphaned

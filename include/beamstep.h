@@ -335,6 +335,26 @@ int bs_get_finished(bs_state *h, float *norm, float *raw, int32_t *len,
 /* Steps taken since bs_create or bs_reset (host value, no GPU work). */
 int bs_steps_taken(const bs_state *h);
 
+/* Checkpoint and resume (a search moved to another handle, process or device):
+ * a snapshot holds the search state -- running scores, slot ranks, done flags,
+ * finished sets, the backpointers of the steps taken, the last selection and
+ * the reorder plan -- behind a header naming the configuration and the steps
+ * taken. It holds values only (no addresses), in host memory the caller owns.
+ * bs_state_size: the snapshot's size in bytes (host int64).
+ * bs_state_save: synchronises the handle's stream and copies the snapshot into
+ *   dst (host, at least bs_state_size bytes); does not change the handle.
+ * bs_state_load: restores a snapshot into a handle created with the same
+ *   bs_config (every field; the device may differ), then synchronises; the
+ *   next bs_step is step (steps taken in the snapshot) + 1, and bs_reorder_kv
+ *   uses the snapshot's last plan. The KV cache itself is the caller's (save
+ *   it alongside); a paged cache attached to the handle is not part of the
+ *   snapshot, and refuses further reorders (BS_ESTATE) until it is reset.
+ * Errors: BS_EINVAL (NULL pointer, too small a buffer, a snapshot of another
+ * configuration or a corrupt header); BS_EDEVICE. */
+int bs_state_size(const bs_state *h, int64_t *bytes);
+int bs_state_save(bs_state *h, void *dst, int64_t capacity);
+int bs_state_load(bs_state *h, const void *src, int64_t size);
+
 /* Frees the handle's device buffers after synchronising its stream. */
 void bs_destroy(bs_state *h);
 

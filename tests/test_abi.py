@@ -11,7 +11,7 @@ import beam_search_step_amd as bs
 
 def test_library_exports_every_declared_function():
     names = bs.declared_functions()
-    assert len(names) == 22
+    assert len(names) == 25
     lib = bs.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, f"not exported: {missing}"
@@ -66,6 +66,9 @@ def test_null_arguments_are_rejected():
     assert L.bs_reset(None) == bs.BS_EINVAL
     assert L.bs_verify(None, None, 0, None, None, None) == bs.BS_EINVAL
     assert L.bs_verify_noalloc(None, None, 0, 1, 1, 10, 10, None, None, None) == bs.BS_EINVAL
+    assert L.bs_state_size(None, None) == bs.BS_EINVAL
+    assert L.bs_state_save(None, None, 0) == bs.BS_EINVAL
+    assert L.bs_state_load(None, None, 0) == bs.BS_EINVAL
     h = ctypes.c_void_p()
     assert L.bs_verify_create(0, 8, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL
     assert L.bs_verify_create(2, 65, 100, 0, None, ctypes.byref(h)) == bs.BS_EINVAL

@@ -598,6 +598,62 @@ def test_rejected_calls_enqueue_nothing(dev):
     g.close()
 
 
+def test_checkpoint_and_resume(dev):
+    """A snapshot taken at step 12 of a Transformer-base-shaped search (EOS
+    reachable, items finishing) and loaded into a new handle continues the
+    search exactly: every later step's outputs, selections and finished sets,
+    the final hypotheses, and the first KV reorder after the load (which uses
+    the snapshot's plan) are the same bits as the uninterrupted search's. A
+    snapshot is refused by a handle of another configuration."""
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["tbase"].replace(batch=4, max_steps=70, num_return=2)
+    k = 12
+    lgs = [to_device(synth.logits(wl, t), dev) for t in range(1, wl.max_steps + 1)]
+    words = wl.kv_bytes_per_pos // 4
+    kv0 = torch.from_numpy(np.random.default_rng(5).integers(-2 ** 31, 2 ** 31 - 1,
+                           size=(wl.rows, 3, words), dtype=np.int32)).to(dev)
+
+    def run(g, t0, snapshot_at=None):
+        outs, snap, kv_after = [], None, None
+        for t in range(t0, wl.max_steps + 1):
+            bi, tk, sc, dn = g.step(lgs[t - 1])
+            j, c = g.selection()
+            outs.append([x.cpu().numpy().copy() for x in (bi, tk, sc, dn, j, c, *g.finished())])
+            if t == snapshot_at:
+                snap = g.save()
+                kv = kv0.clone()
+                g.reorder_kv([kv], 3)
+                kv_after = kv.cpu().numpy()
+            if dn.cpu().numpy().all():
+                break
+        outs.append([x.cpu().numpy() for x in g.finalize()])
+        return outs, snap, kv_after
+
+    a = bs.BeamSearch.for_workload(wl)
+    full, snap, kv_a = run(a, 1, snapshot_at=k)
+    assert snap is not None and a.steps > k + 5, "the search ended too early to test a resume"
+    a.close()
+    b = bs.BeamSearch.for_workload(wl)
+    b.load(snap)
+    assert b.steps == k
+    kv = kv0.clone()
+    b.reorder_kv([kv], 3)                     # step k's plan, from the snapshot
+    assert np.array_equal(kv.cpu().numpy(), kv_a)
+    resumed, _, _ = run(b, k + 1)
+    assert len(resumed) == len(full) - k
+    for x, y in zip(full[k:], resumed):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v, equal_nan=True)
+    b.close()
+    other = bs.BeamSearch.for_workload(wl.replace(max_steps=71))
+    with pytest.raises(bs.BeamStepError) as e:
+        other.load(snap)
+    assert e.value.status == bs.BS_EINVAL and other.steps == 0
+    with pytest.raises(bs.BeamStepError):
+        other.load(snap[:100])
+    other.close()
+
+
 def test_wrappers_reject_bad_tensors_before_launching(dev):
     """The Python wrappers refuse tensors a kernel would read or write out of
     bounds, before any launch; the handle's state is unchanged."""
