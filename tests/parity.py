@@ -104,7 +104,7 @@ def device_filler(wl, dev):
 
 def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_finished=True,
                  rep=None, tile_elems=0, prune="topw", select="fused", other_rows="synth",
-                 kv_check_every=1):
+                 kv_check_every=1, select_check_every=1):
     """Run ``steps`` decode steps of workload ``wl`` on the GPU with the oracle
     following along on ``items`` (default: all; items are independent, so a
     sample of them can be followed at full batch size). With ``kv_planes`` > 0
@@ -116,7 +116,13 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     one). ``other_rows="device"`` generates only the followed items' logits on
     the host (the workload's generator) and draws the other rows on the GPU
     (``device_filler``); ``kv_check_every`` compares the followed rows' KV
-    every that many steps (and at the last). Returns (Report, gpu search,
+    every that many steps (and at the last). ``select_check_every`` > 1 (with
+    ``other_rows="device"``) compares the selection with the oracle's own only
+    at step 1, every that many steps and the last step, where the followed
+    rows' logits come from the workload's generator; at the other steps every
+    row is drawn on the GPU and the oracle applies the library's selection, so
+    that beam_idx, tokens, scores, done flags, finished hypotheses and the KV
+    cache are still compared at every step. Returns (Report, gpu search,
     oracle search)."""
     import torch
     import beam_search_step_amd as bs
@@ -139,12 +145,15 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
     planes = [torch.zeros((wl.rows, steps, words), dtype=torch.int32, device=dev)
               for _ in range(kv_planes)]
     host = [np.zeros((len(rows), steps, words), np.int32) for _ in range(kv_planes)]
+    assert select_check_every == 1 or other_rows == "device"
     for t in range(1, steps + 1):
         where = f"{wl.name} t={t}"
+        check = t == 1 or t == steps or t % select_check_every == 0
         if other_rows == "device":
-            lg_rows = synth.logits(wl, t, rows=rows.tolist())
             x = fill(t)
-            x[rows_dev] = to_device(lg_rows, dev)
+            if check:
+                lg_rows = synth.logits(wl, t, rows=rows.tolist())
+                x[rows_dev] = to_device(lg_rows, dev)
         else:
             lg = logits_fn(t)
             x = to_device(lg, dev)
@@ -153,11 +162,12 @@ def run_stepwise(wl, steps, dev, items=None, logits_fn=None, kv_planes=0, check_
         gj, gc = gpu.selection()
         gj, gc = gj.cpu().numpy(), gc.cpu().numpy()
         bi, tk, sc, dn = (x.cpu().numpy() for x in (bi, tk, sc, dn))
-        oj, oc, on = ref.select(lg_rows)
-        for k, b in enumerate(items):
-            check_selection((oj[k], oc[k], on[k]),
-                            lambda js, k=k: ref.cand_scores(lg_rows, k, js),
-                            gj[b], gc[b], K, rep, f"{where} item {b}")
+        if check:
+            oj, oc, on = ref.select(lg_rows)
+            for k, b in enumerate(items):
+                check_selection((oj[k], oc[k], on[k]),
+                                lambda js, k=k: ref.cand_scores(lg_rows, k, js),
+                                gj[b], gc[b], K, rep, f"{where} item {b}")
         obi, otk, osc, odn = ref.apply(gj[sub].astype(np.int64), gc[sub])
         assert (bi[sub] == obi).all(), f"{where}: beam_idx {bi[sub]} vs {obi}"
         assert (tk[sub] == otk).all(), f"{where}: token_id {tk[sub]} vs {otk}"

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from parity import Report, check_selection, kv_position, to_device
+from parity import Report, check_selection, device_filler, kv_position, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -36,21 +36,37 @@ def log(msg):
 
 
 def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits_fn=None,
-              select="fused", second_cache=False):
+              select="fused", second_cache=False, items=None):
     """Teacher-forced search of ``steps`` steps with a paged cache of
     ``kv_planes`` pools; returns (Report, copies made, steps run).
 
     With the fused selection the step's table update runs inside bs_step for
     the first cache of a handle; with the two-pass selection, or for a second
     cache of the same handle (``second_cache``: another cache is created first
-    and never reordered), the reorder call launches it."""
+    and never reordered), the reorder call launches it.
+
+    ``items`` (default: all) are the items the oracle follows: their
+    selections, beam_idx and done flags are compared with it. The other items'
+    logits are then drawn on the GPU (``device_filler``), and their host copy of
+    the cache follows the library's own beam_idx and done flags, so that the
+    block tables and the paged content of every item are still checked at every
+    step."""
     import beam_search_step_amd as bs
 
-    logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     rep = Report()
     B, W = wl.batch, wl.beam
+    items = list(range(B)) if items is None else list(items)
+    sub = np.array(items)
+    every = len(items) == B
+    if every:
+        logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
+    else:
+        assert logits_fn is None
+        fill = device_filler(wl, dev)
+        frows = np.array([b * W + w for b in items for w in range(W)])
+        frows_dev = torch.from_numpy(frows).to(dev)
     gpu = bs.BeamSearch.for_workload(wl, select=select)
-    ref = oracle.Search.for_workload(wl)
+    ref = oracle.Search.for_workload(wl.replace(batch=len(items)))
     first = bs.PagedKV(gpu, block_size, blocks_per_item) if second_cache else None
     pk = bs.PagedKV(gpu, block_size, blocks_per_item)
     bpi = pk.blocks_per_item
@@ -75,26 +91,36 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
             pools[li][torch.from_numpy(phys).long().to(dev), (t - 1) % block_size] = \
                 torch.from_numpy(vals).to(dev)
             host[li][rows, t - 1] = vals
-        lg = logits_fn(t)
-        bi, tk, sc, dn = gpu.step(to_device(lg, dev))
+        if every:
+            lg = logits_fn(t)
+            x = to_device(lg, dev)
+        else:
+            lg = synth.logits(wl, t, rows=frows.tolist())
+            x = fill(t)
+            x[frows_dev] = to_device(lg, dev)
+        bi, tk, sc, dn = gpu.step(x)
         gj, gc = gpu.selection()
         gj, gc = gj.cpu().numpy(), gc.cpu().numpy()
+        bi, sc, dn = bi.cpu().numpy(), sc.cpu().numpy(), dn.cpu().numpy().astype(bool)
         oj, oc, on = ref.select(lg)
-        for b in range(B):
-            check_selection((oj[b], oc[b], on[b]), lambda js, b=b: ref.cand_scores(lg, b, js),
+        for k, b in enumerate(items):
+            check_selection((oj[k], oc[k], on[k]), lambda js, k=k: ref.cand_scores(lg, k, js),
                             gj[b], gc[b], gpu.K, rep, f"{where} item {b}")
-        obi, otk, osc, odn = ref.apply(gj.astype(np.int64), gc)
-        assert (bi.cpu().numpy() == obi).all(), f"{where}: beam_idx"
-        assert (dn.cpu().numpy().astype(bool) == odn).all(), f"{where}: done"
+        obi, otk, osc, odn = ref.apply(gj[sub].astype(np.int64), gc[sub])
+        assert (bi[sub] == obi).all(), f"{where}: beam_idx"
+        assert np.array_equal(sc[sub], osc), f"{where}: scores"
+        assert (dn[sub] == odn).all(), f"{where}: done"
         pk.reorder(desc, t)
-        oracle.kv_reorder(host, obi, odn, t)
-        live = (osc > -np.inf) & ~odn[:, None]
+        # the followed items' beam_idx, scores and done flags equal the
+        # oracle's (asserted above); the others are the library's own
+        oracle.kv_reorder(host, bi.astype(np.int64), dn, t)
+        live = (sc > -np.inf) & ~dn[:, None]
         # copies made this step: live slots beyond the first child of each
         # parent, when position t falls inside a block
         if t % block_size:
             for b in range(B):
                 lv = np.flatnonzero(live[b])
-                copies += len(lv) - len(set(obi[b, lv].tolist()))
+                copies += len(lv) - len(set(bi[b, lv].tolist()))
         table = pk.table().cpu().numpy()
         ov, free = pk.status()
         assert ov == 0, f"{where}: pool overflow"
@@ -117,7 +143,7 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
                     assert np.array_equal(got[li][ph, pos % block_size], host[li][r, :t]), \
                         f"{where} item {b} slot {w} plane {li}: paged content differs"
         t_run = t
-        if odn.all():
+        if dn.all():
             break
     pk.close()
     if first is not None:
@@ -189,6 +215,17 @@ def test_llama3_8b_shape_paged(dev):
     rep, copies, t = run_paged(wl, 40, dev, 16, kv_planes=4)
     log(f"llama3_8b paged: {t} steps, {copies} copies, {rep}")
     assert t == 40 and copies > 0
+
+
+def test_llama3_8b_paged_full_search(dev):
+    # the whole search the paged benchmark times (200 steps, blocks of 16
+    # positions, the default pool of W * ceil(200 / 16) blocks per item): items
+    # 2 and 7 followed by the oracle, every item's tables and the content of
+    # every live row checked at every step; two pools keep the host copy small
+    wl = synth.WORKLOADS["llama3_8b"]
+    rep, copies, t = run_paged(wl, wl.max_steps, dev, 16, kv_planes=2, items=[2, 7])
+    log(f"llama3_8b paged, whole search: {t} steps, {copies} copies, {rep}")
+    assert t == wl.max_steps and copies > 0
 
 
 def test_paged_overflow_is_reported(dev):

@@ -158,6 +158,23 @@ def test_wide_beam_twenty_steps(dev):
     g.close()
 
 
+def test_wide_beam_full_search(dev):
+    """The wide search for all 256 steps: items 3 and 12 followed by the
+    oracle, their selections compared at step 1, every 16th step and the last;
+    beam_idx, tokens, scores, done flags and finished hypotheses at every step;
+    two KV planes of 4 KiB per position (gen_len up to 256, the reorder's
+    W = 16 kernel on the late steps' full regions) every 32 steps; then the
+    final hypotheses."""
+    wl = synth.WORKLOADS["wide"]
+    items = [3, 12]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=2,
+                               other_rows="device", kv_check_every=32, select_check_every=16)
+    assert rep.steps == wl.max_steps and rep.compared == 2 * 17
+    compare_final(g, ref, items, wl.num_return, "wide, 256 steps")
+    log(f"wide full search: {rep}")
+    g.close()
+
+
 def test_llama3_8b_with_reachable_eos(dev):
     """The Llama-shaped workload with EOS = 1 outside the Zipf term and a
     rising EOS bias, so that the EOS path and early stopping run at V=128256."""
