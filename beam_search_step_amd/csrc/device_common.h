@@ -11,7 +11,6 @@ constexpr int kWaves = kThreads / 64;   // wave64
 constexpr int kMaxBeam = 16;
 constexpr int kMaxGridRows = 65535;     // rows per launch: the grid's y extent
 constexpr int kListCap = 1024;          // LDS candidate list of the top-W
-constexpr int kGroups = kThreads / 16;  // 16-lane groups for the selection bound
 constexpr int kMergeNE = 8;             // K2 candidates per thread per batch
 constexpr int kPlanStride = 64;         // int32 words per item of the KV plan
 constexpr int kK3Threads = 256;         // threads per KV-reorder workgroup

@@ -59,13 +59,13 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
   // its first store: s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their
   // no-wait maxima).
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  // After that wait the stores to every destination slot issue back to back,
-  // with no wait between slots. With each step's reorder on a cold cache,
-  // waiting for the stores after every slot, every second, fourth or eighth
-  // slot was never faster: within 1% at W = 4 (Llama-3-8B shape), and at
-  // W = 16 (V = 250000) 5.69-5.74 TB/s with no wait against 5.58-5.60 after
-  // every fourth slot and 5.17-5.22 after every slot. Only the wait above,
-  // before the first store, matters for correctness.
+  // Between destination slots: for W <= 4 a thread waits for its stores after
+  // each slot; for wider beams the stores to all slots issue back to back.
+  // Measured with each step's reorder on a cold cache: at W = 16 (V = 250000)
+  // 5.69-5.74 TB/s with no wait against 5.58-5.60 after every fourth slot and
+  // 5.17-5.22 after every slot; at W = 4 (Llama-3-8B shape, three runs each)
+  // 5.81-5.88 TB/s waiting after every slot against 5.78-5.86 with no wait.
+  // Only the wait above, before the first store, matters for correctness.
 #pragma unroll
   for (int q = 0; q < WMAX; ++q) {
     for (int m = dmask[q]; m; m &= m - 1) {
@@ -75,6 +75,7 @@ __device__ __forceinline__ void move_words(char* base, int64_t row0, int64_t row
 #pragma unroll
       for (int k = 0; k < NP; ++k)
         if (ok[k]) __builtin_nontemporal_store(v[k][q], reinterpret_cast<WT*>(dst + off[k]));
+      if constexpr (WMAX <= 4) __builtin_amdgcn_s_waitcnt(0x0F70);
     }
   }
 }

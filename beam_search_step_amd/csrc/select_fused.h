@@ -26,29 +26,39 @@ struct K1Args {
   int* pv;              // [rows][tiles][WMAX] their columns
 };
 
-// tau for a tile: the w_keep-th largest of the kGroups group maxima, which is
-// a lower bound on the tile's w_keep-th best logit (the group maxima are
-// distinct elements). Every wave computes it on its own: lane l of each
-// 16-lane row holds gmax[l % 16] and counts, over the 15 DPP row rotations,
-// how many of the others are larger (gt) and at least as large (ge). A value
-// with gt <= w-1 and ge+1 >= w is the w-th largest; all such lanes hold the
-// same value, so the rotation direction does not matter.
+// tau for a tile: the w_keep-th largest of the tile's G group maxima (16
+// groups of 16 lanes, or 32 groups of 8 lanes), which is a lower bound on the
+// tile's w_keep-th best logit (the group maxima are distinct elements). Every
+// wave computes it on its own: lane l holds gmax[l % G] and counts, over the
+// 15 DPP rotations of its 16-lane row (and for G = 32 over the 16 rotations
+// of the other half's values, gmax[(l % 32) ^ 16]), how many of the others
+// are larger (gt) and at least as large (ge). A value with gt <= w-1 and
+// ge+1 >= w is the w-th largest; all such lanes hold the same value, so the
+// rotation direction does not matter.
 template <int R>
-__device__ __forceinline__ void rank_rotations(float g, int& gt, int& ge) {
+__device__ __forceinline__ void count_rotations(float h, float g, int& gt, int& ge) {
   if constexpr (R <= 15) {
-    const float o = dpp_f<0x120 + R>(g);  // row_ror:R
+    const float o = dpp_f<0x120 + R>(h);  // row_ror:R
     gt += o > g ? 1 : 0;
     ge += o >= g ? 1 : 0;
-    rank_rotations<R + 1>(g, gt, ge);
+    count_rotations<R + 1>(h, g, gt, ge);
   }
 }
 
+template <int G>
 __device__ __forceinline__ float tile_tau(const float* gmax, int w_keep) {
+  static_assert(G == 16 || G == 32, "16 or 32 group maxima");
   const int lane = threadIdx.x & 63;
-  const float g = gmax[lane & 15];
+  const float g = gmax[lane & (G - 1)];
   int gt = 0, ge = 0;
-  rank_rotations<1>(g, gt, ge);
-  const uint64_t q = __ballot(lane < 16 && gt <= w_keep - 1 && ge + 1 >= w_keep);
+  count_rotations<1>(g, g, gt, ge);
+  if constexpr (G == 32) {
+    const float h = gmax[(lane & 31) ^ 16];
+    gt += h > g ? 1 : 0;
+    ge += h >= g ? 1 : 0;
+    count_rotations<1>(h, g, gt, ge);
+  }
+  const uint64_t q = __ballot(lane < G && gt <= w_keep - 1 && ge + 1 >= w_keep);
   const int l = __builtin_ctzll(q);
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), l));
 }
@@ -56,7 +66,14 @@ __device__ __forceinline__ float tile_tau(const float* gmax, int w_keep) {
 template <int WMAX, typename T, int EPT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   constexpr int kRegion = kListCap / kWaves;  // candidate slots of one wave
-  __shared__ float gmax[kGroups];
+  // group maxima for tau: 16 groups of 256 threads / 16 lanes, or 32 of 8
+  // lanes when up to 16 candidates are kept. At K = 16 a bound from 16 maxima
+  // is their minimum and lets ~54 logits of a 16384-logit tile through to the
+  // ranking (Gaussian logits); from 32 maxima ~22. Measured at W = 16, V =
+  // 250000: K1 + K2 65.2 us against 69.9 per step. For K <= 4 the count is
+  // ~4.4 with 16 groups already.
+  constexpr int kG = WMAX >= 16 ? 32 : 16;
+  __shared__ float gmax[kG];
   __shared__ float wm[kWaves], ws[kWaves];
   __shared__ int wn[kWaves];
   __shared__ float rx[kWaves];
@@ -89,9 +106,14 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   for (int i = 0; i < EPT; ++i) m = fmaxf(m, x[i]);
   m = fmaxf(m, dpp_f<0xb1>(m));   // quad_perm [1,0,3,2]
   m = fmaxf(m, dpp_f<0x4e>(m));   // quad_perm [2,3,0,1]
-  m = fmaxf(m, dpp_f<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_f<0x141>(m));  // row_half_mirror: every lane has its 8-lane half's max
+  if constexpr (kG == 32) {
+    if ((lane & 7) == 0) gmax[tid >> 3] = m;
+  }
   m = fmaxf(m, dpp_f<0x140>(m));  // row_mirror: every lane has its row's max
-  if ((lane & 15) == 0) gmax[tid >> 4] = m;
+  if constexpr (kG == 16) {
+    if ((lane & 15) == 0) gmax[tid >> 4] = m;
+  }
   const float mw = fmaxf(
       fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
@@ -115,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void k1_expand_select(K1Args a) {
   // prune, stage 1: list every logit >= tau in this wave's LDS region as a
   // key that orders by (logit desc, column asc) (ballot + mbcnt compaction, no
   // atomics); -inf is never a candidate
-  float tau = tile_tau(gmax, K);
+  float tau = tile_tau<kG>(gmax, K);
   if (!(tau > -kInf)) tau = -3.402823466e38f;
   int woff = 0;
 #pragma unroll
