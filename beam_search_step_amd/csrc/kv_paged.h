@@ -189,7 +189,10 @@ struct K7Args {
 // store. The grid is sized so that a workgroup rarely takes more than one
 // unit (1024 measured 11% faster per step than 256 with blocks of 16
 // positions, 18% with blocks of 32; 2048 no faster), since a workgroup's next
-// unit waits for its previous stores.
+// unit waits for its previous stores. Loads and stores carry the nontemporal
+// hint, as the contiguous reorder's do (every word is read once and written
+// once): 42,588-42,856 beam steps/s against 40,534-40,821 with plain ones at
+// the Llama-3-8B shape (blocks of 16, three runs each).
 constexpr int kCopyPlanes = 8;
 constexpr int kCopyGrid = 1024;
 template <int WORD>
@@ -212,10 +215,10 @@ __global__ __launch_bounds__(kThreads) void k7_paged_copy(K7Args a) {
     WT v[kCopyPlanes];
 #pragma unroll
     for (int k = 0; k < kCopyPlanes; ++k)
-      if (k < np) v[k] = *reinterpret_cast<const WT*>(a.pools[p0 + k] + so);
+      if (k < np) v[k] = __builtin_nontemporal_load(reinterpret_cast<const WT*>(a.pools[p0 + k] + so));
 #pragma unroll
     for (int k = 0; k < kCopyPlanes; ++k)
-      if (k < np) *reinterpret_cast<WT*>(a.pools[p0 + k] + d) = v[k];
+      if (k < np) __builtin_nontemporal_store(v[k], reinterpret_cast<WT*>(a.pools[p0 + k] + d));
   }
 }
 
