@@ -71,6 +71,22 @@ def test_two_pass_llama3_8b_sampled(dev):
     g.close()
 
 
+def test_two_pass_llama3_8b_full_search(dev):
+    """The two-pass selection over the whole 200-step Llama-shaped search:
+    items 1 and 6 followed, their selections compared at step 1, every 10th
+    step and the last, everything else at every step; then the final
+    hypotheses."""
+    wl = synth.WORKLOADS["llama3_8b"]
+    items = [1, 6]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=1,
+                               select="two_pass", other_rows="device", kv_check_every=25,
+                               select_check_every=10)
+    assert rep.steps == wl.max_steps and rep.compared == 2 * 21
+    compare_final(g, ref, items, wl.num_return, "two-pass llama3_8b, 200 steps")
+    log(f"two-pass llama3_8b full search: {rep}")
+    g.close()
+
+
 def test_two_pass_llama3_reachable_eos_top2w(dev):
     wl = synth.WORKLOADS["llama3_8b"].replace(batch=3, eos_id=1, eos_in_zipf=False,
                                               eos_ramp=14.0, ramp_steps=10, max_steps=20)
@@ -83,6 +99,21 @@ def test_two_pass_wide_sampled(dev):
     wl = synth.WORKLOADS["wide"]
     rep, g, ref = run_stepwise(wl, 3, dev, items=[4, 11], kv_planes=1, select="two_pass")
     log(f"two-pass wide: {rep}")
+    g.close()
+
+
+def test_two_pass_wide_full_search(dev):
+    """The two-pass selection over the whole 256-step wide search: items 4 and
+    11 followed, their selections compared at step 1, every 16th step and the
+    last, everything else at every step; then the final hypotheses."""
+    wl = synth.WORKLOADS["wide"]
+    items = [4, 11]
+    rep, g, ref = run_stepwise(wl, wl.max_steps, dev, items=items, kv_planes=1,
+                               select="two_pass", other_rows="device", kv_check_every=64,
+                               select_check_every=16)
+    assert rep.steps == wl.max_steps and rep.compared == 2 * 17
+    compare_final(g, ref, items, wl.num_return, "two-pass wide, 256 steps")
+    log(f"two-pass wide full search: {rep}")
     g.close()
 
 
