@@ -123,12 +123,13 @@ size_t align_up(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int choose_ept(int rows, int V, int hint) {
   if (hint == 16 || hint == 32 || hint == 64) return hint;
-  // the largest per-thread tile that still gives >= 1024 workgroups
-  for (int e : {64, 32}) {
-    const int64_t tiles = (V + (int64_t)kThreads * e - 1) / ((int64_t)kThreads * e);
-    if ((int64_t)rows * tiles >= 1024) return e;
-  }
-  return 16;
+  // 32 logits per thread when that still gives >= 1024 workgroups, else 16.
+  // At the wide shape (256 rows, V = 250000) K1 + K2 took 60.6 us per step
+  // with 32, 64.8 with 64 and 84 with 16 (62 tiles per row lengthen K2's
+  // merge); the Llama-3-8B and Transformer-base shapes get 16 (32 gives 512
+  // workgroups there and measured no faster).
+  const int64_t tiles32 = (V + (int64_t)kThreads * 32 - 1) / ((int64_t)kThreads * 32);
+  return (int64_t)rows * tiles32 >= 1024 ? 32 : 16;
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? BS_OK : BS_EDEVICE; }
@@ -693,10 +694,25 @@ int bs_step(bs_state* h, const void* logits, int64_t row_stride_elems, int32_t* 
   return BS_OK;
 }
 
+// n * stride + bytes <= limit, without overflow (all >= 0)
+static bool span_within(int64_t n, int64_t stride, int64_t bytes, int64_t limit) {
+  if (bytes > limit) return false;
+  return n == 0 || stride <= (limit - bytes) / n;
+}
+
 static int reorder_kv(bs_state* h, const bs_kv_desc* kv, int32_t gen_len, LaunchEvents ev) {
   if (!h || !kv || !kv->planes || kv->n_planes < 1 || gen_len < 0) return BS_EINVAL;
   if (kv->bytes_per_pos <= 0 || kv->row_stride <= 0 || kv->pos_stride <= 0 || kv->pos_offset < 0)
     return BS_EINVAL;
+  // the moved (row, position) pairs of a plane must not share bytes: positions
+  // apart within a row, and either rows apart by the moved span of a row
+  // (row-major) or positions apart by every row (position-major)
+  const int64_t rows = (int64_t)h->B * h->W;
+  const bool row_major = span_within(gen_len > 0 ? gen_len - 1 : 0, kv->pos_stride,
+                                     kv->bytes_per_pos, kv->row_stride);
+  const bool pos_major = kv->bytes_per_pos <= kv->row_stride &&
+                         span_within(rows - 1, kv->row_stride, kv->bytes_per_pos, kv->pos_stride);
+  if (kv->bytes_per_pos > kv->pos_stride || !(row_major || pos_major)) return BS_EINVAL;
   if (h->t == 0) return BS_ESTATE;
   if (gen_len == 0) {  // nothing to launch: the events are recorded back to back
     if ((ev.start && hipEventRecord(ev.start, h->stream) != hipSuccess) ||
@@ -988,8 +1004,8 @@ struct SnapHeader {
   double alpha;
   uint64_t state_bytes;
 };
-size_t state_bytes(const bs_state* h) { return (size_t)((const char*)h->lpt - (const char*)h->block); }
-SnapHeader snap_header(const bs_state* h) {
+static size_t state_bytes(const bs_state* h) { return (size_t)((const char*)h->lpt - (const char*)h->block); }
+static SnapHeader snap_header(const bs_state* h) {
   SnapHeader x;
   memset(&x, 0, sizeof(x));
   x.magic = kSnapMagic;

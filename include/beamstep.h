@@ -198,7 +198,12 @@ typedef struct {
  * Requires bytes_per_pos, row_stride, pos_stride, pos_offset*pos_stride and
  * every plane address to be multiples of 4 bytes (16 for the fast path), and
  * a row's gen_len * bytes_per_pos to be under 2^32 copy words (of 16 bytes on
- * the fast path, 4 otherwise).
+ * the fast path, 4 otherwise). The moved (row, position) pairs of a plane
+ * must not share bytes: bytes_per_pos <= pos_stride, and either rows lie a
+ * whole moved span apart, (gen_len-1)*pos_stride + bytes_per_pos <=
+ * row_stride (rows outermost), or positions lie all rows apart,
+ * (B*W-1)*row_stride + bytes_per_pos <= pos_stride with bytes_per_pos <=
+ * row_stride (positions outermost); other layouts are refused.
  * Errors: BS_EINVAL; BS_ESTATE before the first bs_step; BS_EDEVICE. */
 int bs_reorder_kv(bs_state *h, const bs_kv_desc *kv, int32_t gen_len);
 

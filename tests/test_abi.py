@@ -22,6 +22,10 @@ def test_exports_match_header_exactly():
                          text=True, check=True).stdout
     exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T bs_" in ln})
     assert exported == bs.declared_functions()
+    # no other function leaves the library (helpers have internal linkage)
+    others = [ln.split()[-1] for ln in out.splitlines()
+              if ln.split()[-2] in ("T", "W") and not ln.split()[-1].startswith("bs_")]
+    assert not others, f"exported helpers: {others}"
 
 
 def test_library_is_built_for_gfx950():

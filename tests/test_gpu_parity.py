@@ -186,11 +186,12 @@ def test_llama3_8b_with_reachable_eos(dev):
     g.close()
 
 
-@pytest.mark.parametrize("tile_elems", [0, 16, 32])
+@pytest.mark.parametrize("tile_elems", [0, 16, 64])
 def test_wide_beam_sampled_items(dev, tile_elems):
     """B=16, W=16, V=250000 fp32 (top-16 of 4.0M per item), 3 steps, items 3
-    and 12. tile_elems=16 gives 62 tiles per row, so the merge runs in several
-    batches; 32 gives 31 tiles of 8192 logits."""
+    and 12. The library picks 32 logits per thread here (31 tiles of 8192
+    logits per row); 16 gives 62 tiles per row, so the merge runs in several
+    batches; 64 gives 16 tiles of 16384."""
     wl = synth.WORKLOADS["wide"]
     rep, g, ref = run_stepwise(wl, 3, dev, items=[3, 12], kv_planes=1, tile_elems=tile_elems)
     log(f"wide tile={tile_elems}: {rep}")
@@ -561,7 +562,8 @@ def test_rejected_calls_enqueue_nothing(dev):
     """BS_EINVAL and BS_ESTATE are decided on the host before any launch: a
     step with a NULL output leaves the step count and the next step as they
     were; a reorder over 130 planes (two launches) whose last plane pointer is
-    NULL, or whose plane address is not 4-byte aligned, moves nothing in any
+    NULL, whose plane address is not 4-byte aligned, or whose layout would
+    give two (row, position) pairs the same bytes, moves nothing in any
     plane; a paged reorder with a NULL pool or the wrong gen_len leaves the
     block table as it was; a step past max_steps is refused."""
     import beam_search_step_amd as bs
@@ -584,6 +586,12 @@ def test_rejected_calls_enqueue_nothing(dev):
     odd = bs.make_kv_desc(planes)
     odd._keep[0] = raw.data_ptr() + 2          # not a multiple of 4 bytes
     assert L.bs_reorder_kv(g.h, ctypes.byref(odd), 1) == bs.BS_EINVAL
+    lap = bs.make_kv_desc(planes)              # positions 16 bytes long, 8 apart
+    lap.pos_stride = 8
+    assert L.bs_reorder_kv(g.h, ctypes.byref(lap), 1) == bs.BS_EINVAL
+    lap = bs.make_kv_desc(planes)              # rows 8 bytes apart, neither layout
+    lap.row_stride = 8
+    assert L.bs_reorder_kv(g.h, ctypes.byref(lap), 1) == bs.BS_EINVAL
     torch.cuda.synchronize()
     assert all(torch.equal(p, q) for p, q in zip(planes, before)), "a refused reorder moved rows"
     assert raw.count_nonzero().item() == 0
@@ -767,6 +775,8 @@ KV_LAYOUTS = {
     "w16_prompt": (8, 0, 5, 2),
     "w4_padded_prompt": (3, 2, 3, 3),
     "w16_130_planes": (4, 0, 0, 130),
+    # positions outermost: each plane is [positions][rows][words + pad]
+    "position_major": (3, 1, 2, 2, True),
 }
 
 
@@ -801,7 +811,8 @@ def test_kv_reorder_timed(dev, layout):
 
 def _kv_layout_case(dev, layout, W, timed):
     import beam_search_step_amd as bs
-    words, pad, P, n_planes = KV_LAYOUTS[layout]
+    words, pad, P, n_planes, *rest = KV_LAYOUTS[layout]
+    pos_major = bool(rest and rest[0])
     B, V, T = 3, 40, 7
     rows = B * W
     wl = synth.WORKLOADS["toy"].replace(batch=B, beam=W, vocab=V, eos_id=-1, stop="never",
@@ -811,8 +822,13 @@ def _kv_layout_case(dev, layout, W, timed):
     rng = np.random.default_rng(words * 100 + pad * 10 + P + W)
     full0 = [rng.integers(-2 ** 31, 2 ** 31 - 1, size=(rows, P + T, words + pad), dtype=np.int64)
              .astype(np.int32) for _ in range(n_planes)]
-    full = [torch.from_numpy(f).to(dev) for f in full0]
+    if pos_major:   # device storage [positions][rows][...], seen as [rows][positions][...]
+        full = [torch.from_numpy(np.ascontiguousarray(f.transpose(1, 0, 2))).to(dev)
+                .permute(1, 0, 2) for f in full0]
+    else:
+        full = [torch.from_numpy(f).to(dev) for f in full0]
     desc = bs.make_kv_desc([f[:, :, :words] for f in full], pos_offset=P)
+    assert (desc.pos_stride > desc.row_stride) == pos_major
     host = [np.ascontiguousarray(f[:, :, :words]) for f in full0]
     for t in range(1, T + 1):
         lg = synth.logits(wl, t)
