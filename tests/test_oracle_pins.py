@@ -470,8 +470,8 @@ def test_selection_ties_bf16(orc):
 
 def test_tbase_eos_schedule_finish_median(orc):
     """The Transformer-base workload's EOS schedule (its start re-tuned so that
-    searches end mid-way, the survey's criterion being a median finish step
-    between 20 and 100): the first 8 items of the search, run by the oracle
+    searches end mid-way, with a median finish step between 20 and 100): the
+    first 8 items of the search, run by the oracle
     to the end, finish at steps whose median lies in that range, none at the
     first steps and none running to the maximum of 128."""
     wl = synth.WORKLOADS["tbase"].replace(batch=8)
