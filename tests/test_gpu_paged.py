@@ -36,7 +36,8 @@ def log(msg):
 
 
 def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits_fn=None,
-              select="fused", second_cache=False, items=None):
+              select="fused", second_cache=False, items=None, select_check_every=1,
+              kv_check_every=1):
     """Teacher-forced search of ``steps`` steps with a paged cache of
     ``kv_planes`` pools; returns (Report, copies made, steps run).
 
@@ -50,7 +51,13 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
     logits are then drawn on the GPU (``device_filler``), and their host copy of
     the cache follows the library's own beam_idx and done flags, so that the
     block tables and the paged content of every item are still checked at every
-    step."""
+    step. With ``select_check_every`` > 1 (and followed items), the selection
+    is compared with the oracle's own only at step 1, every that many steps
+    and the last, where the followed rows' logits come from the workload's
+    generator (every row is drawn on the GPU at the other steps, and the
+    oracle applies the library's selection); ``kv_check_every`` reads the
+    pools back and compares every live row's content every that many steps
+    (and at the last), the tables and block invariants at every step."""
     import beam_search_step_amd as bs
 
     rep = Report()
@@ -58,6 +65,7 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
     items = list(range(B)) if items is None else list(items)
     sub = np.array(items)
     every = len(items) == B
+    assert select_check_every == 1 or not every
     if every:
         logits_fn = logits_fn or (lambda t: synth.logits(wl, t))
     else:
@@ -91,21 +99,24 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
             pools[li][torch.from_numpy(phys).long().to(dev), (t - 1) % block_size] = \
                 torch.from_numpy(vals).to(dev)
             host[li][rows, t - 1] = vals
+        check = t == 1 or t == steps or t % select_check_every == 0
         if every:
             lg = logits_fn(t)
             x = to_device(lg, dev)
         else:
-            lg = synth.logits(wl, t, rows=frows.tolist())
             x = fill(t)
-            x[frows_dev] = to_device(lg, dev)
+            if check:
+                lg = synth.logits(wl, t, rows=frows.tolist())
+                x[frows_dev] = to_device(lg, dev)
         bi, tk, sc, dn = gpu.step(x)
         gj, gc = gpu.selection()
         gj, gc = gj.cpu().numpy(), gc.cpu().numpy()
         bi, sc, dn = bi.cpu().numpy(), sc.cpu().numpy(), dn.cpu().numpy().astype(bool)
-        oj, oc, on = ref.select(lg)
-        for k, b in enumerate(items):
-            check_selection((oj[k], oc[k], on[k]), lambda js, k=k: ref.cand_scores(lg, k, js),
-                            gj[b], gc[b], gpu.K, rep, f"{where} item {b}")
+        if check:
+            oj, oc, on = ref.select(lg)
+            for k, b in enumerate(items):
+                check_selection((oj[k], oc[k], on[k]), lambda js, k=k: ref.cand_scores(lg, k, js),
+                                gj[b], gc[b], gpu.K, rep, f"{where} item {b}")
         obi, otk, osc, odn = ref.apply(gj[sub].astype(np.int64), gc[sub])
         assert (bi[sub] == obi).all(), f"{where}: beam_idx"
         assert np.array_equal(sc[sub], osc), f"{where}: scores"
@@ -125,7 +136,8 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
         ov, free = pk.status()
         assert ov == 0, f"{where}: pool overflow"
         pos = np.arange(t)
-        got = [p.cpu().numpy() for p in pools]
+        content = t % kv_check_every == 0 or t == steps or dn.all()
+        got = [p.cpu().numpy() for p in pools] if content else None
         for b in range(B):
             ids = table[b * W:(b + 1) * W]
             used = ids[ids >= 0]
@@ -136,7 +148,7 @@ def run_paged(wl, steps, dev, block_size, kv_planes=2, blocks_per_item=0, logits
             nxt = ids[lv, t // block_size]
             assert (nxt >= 0).all() and len(set(nxt.tolist())) == len(lv), \
                 f"{where} item {b}: the block for position {t} is not private: {nxt}"
-            for w in lv:
+            for w in lv if content else ():
                 r = b * W + w
                 ph = table[r, pos // block_size]
                 for li in range(kv_planes):
@@ -226,6 +238,18 @@ def test_llama3_8b_paged_full_search(dev):
     rep, copies, t = run_paged(wl, wl.max_steps, dev, 16, kv_planes=2, items=[2, 7])
     log(f"llama3_8b paged, whole search: {t} steps, {copies} copies, {rep}")
     assert t == wl.max_steps and copies > 0
+
+
+def test_wide_paged_full_search(dev):
+    # the wide beam (W = 16, V = 250000 fp32, 4 KiB positions) over its whole
+    # 256-step search with 4 items, blocks of 16: item 1 followed by the
+    # oracle (selections compared every 16 steps), every item's tables and
+    # block invariants at every step, every live row's content every 16 steps
+    wl = synth.WORKLOADS["wide"].replace(batch=4)
+    rep, copies, t = run_paged(wl, wl.max_steps, dev, 16, kv_planes=1, items=[1],
+                               select_check_every=16, kv_check_every=16)
+    log(f"wide paged, whole search: {t} steps, {copies} copies, {rep}")
+    assert t == wl.max_steps and copies > 0 and rep.compared == 17
 
 
 def test_paged_overflow_is_reported(dev):
