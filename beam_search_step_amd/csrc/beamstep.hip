@@ -1061,6 +1061,10 @@ int bs_state_load(bs_state* h, const void* src, int64_t size) {
       hipStreamSynchronize(h->stream) != hipSuccess)
     return BS_EDEVICE;
   h->t = x.steps_taken;
+  // the tables of a paged cache belong to the search before the load: the
+  // step counts that no step can reach make bs_step leave them alone and their
+  // reorders fail with BS_ESTATE until bs_kv_paged_reset
+  for (bs_kv_paged* p = h->caches; p; p = p->next) p->last_t = p->table_t = -2;
   return BS_OK;
 }
 

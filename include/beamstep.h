@@ -353,7 +353,8 @@ int bs_steps_taken(const bs_state *h);
  *   next bs_step is step (steps taken in the snapshot) + 1, and bs_reorder_kv
  *   uses the snapshot's last plan. The KV cache itself is the caller's (save
  *   it alongside); a paged cache attached to the handle is not part of the
- *   snapshot, and refuses further reorders (BS_ESTATE) until it is reset.
+ *   snapshot: after a load it refuses reorders (BS_ESTATE), and bs_step leaves
+ *   its tables alone, until bs_kv_paged_reset.
  * Errors: BS_EINVAL (NULL pointer, too small a buffer, a snapshot of another
  * configuration or a corrupt header); BS_EDEVICE. */
 int bs_state_size(const bs_state *h, int64_t *bytes);

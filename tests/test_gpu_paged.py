@@ -306,3 +306,30 @@ def test_paged_error_paths(dev):
         pk2.reorder(pools, 1)
     assert e.value.status == bs.BS_ESTATE
     pk2.close()
+
+
+def test_paged_reorders_refused_after_a_state_load(dev):
+    # a snapshot restores the search state only: the paged cache of the handle
+    # refuses reorders after the load (even of the very step its tables were
+    # at), until it is reset with the search
+    import beam_search_step_amd as bs
+    wl = synth.WORKLOADS["toy"]
+    g = bs.BeamSearch.for_workload(wl)
+    pk = bs.PagedKV(g, 4)
+    pools = [torch.zeros((wl.batch * pk.blocks_per_item, 4, 8), dtype=torch.int32, device=dev)]
+    g.step(to_device(synth.logits(wl, 1), dev))
+    pk.reorder(pools, 1)
+    snap = g.save()
+    g.load(snap)
+    g.step(to_device(synth.logits(wl, 2), dev))
+    with pytest.raises(bs.BeamStepError) as e:
+        pk.reorder(pools, 2)
+    assert e.value.status == bs.BS_ESTATE
+    g.reset()
+    pk.reset()
+    g.step(to_device(synth.logits(wl, 1), dev))
+    pk.reorder(pools, 1)                       # a new search reorders again
+    ov, free = pk.status()
+    assert ov == 0
+    pk.close()
+    g.close()
