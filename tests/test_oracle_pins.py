@@ -553,6 +553,33 @@ def test_verify_topk_and_min_block(orc):
         orc.verify_ex(lg, prop, top_k=0)
 
 
+def test_verify_topk_against_a_stable_sort(orc):
+    """The rank of each proposal and the accepted lengths on random tied
+    inputs, against an independent definition: the proposal's position in the
+    row sorted by (logit desc, column asc), found by a stable sort; a
+    proposal outside the vocabulary never passes; the accepted length is the
+    longest prefix of passing positions, raised to min_block."""
+    rng = np.random.default_rng(17)
+    B, k, V = 20, 6, 9
+    for trial in range(30):
+        lg = rng.integers(0, 4, size=(B, k, V)).astype(np.float32)   # many ties
+        prop = rng.integers(-1, V + 1, size=(B, k)).astype(np.int32)
+        top_k = int(rng.integers(1, V + 2))
+        min_block = int(rng.integers(0, k + 1))
+        acc, am, rk = orc.verify_ex(lg, prop, top_k=top_k, min_block=min_block)
+        for b in range(B):
+            a, passing = 0, True
+            for i in range(k):
+                p = int(prop[b, i])
+                order = np.lexsort((np.arange(V), -lg[b, i].astype(np.float64)))
+                want_rank = int(np.flatnonzero(order == p)[0]) if 0 <= p < V else V
+                assert rk[b, i] == want_rank, (trial, b, i)
+                assert am[b, i] == order[0]
+                passing = passing and want_rank < top_k
+                a += 1 if passing else 0
+            assert acc[b] == max(a, min_block), (trial, b, top_k, min_block)
+
+
 # ---------------------------------------------------------------------------
 # Hugging Face 2W-candidate variant ("Transformers中的Beam Search高效实现",
 # batched section: 2W candidates, an EOS ranked W or below is skipped, the
