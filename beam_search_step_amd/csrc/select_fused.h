@@ -822,12 +822,29 @@ __device__ __forceinline__ void select_finalize_item(const K2Args& a) {
   } else {  // stage A (W > 4): K rounds per row
     const uint64_t below = ((uint64_t)1 << (lane & 15)) - 1;  // lower lanes of the group
     const int gshift = lane & 48;
+    // The lane's lists wait in LDS (lane-fastest, 64 KB at most) and only each
+    // list's head is in registers: the winning lane reads its next entry, where
+    // a register shift of its lists took ~120 moves a round as compiled. K1 + K2
+    // 58.7 against 60.8 us per step at the wide shape (three runs each). Lists
+    // of H * WMAX > 32 entries (64 tiles of 16 candidates) keep the shift.
+    constexpr bool kLdsLists = H * WMAX <= 32;
+    __shared__ float lsc[kLdsLists ? H * WMAX : 1][kLdsLists ? kThreads : 1];
+    __shared__ int lcol[kLdsLists ? H * WMAX : 1][kLdsLists ? kThreads : 1];
+    int ph[H];
     float hs[H];
     int hc[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) {
+      ph[h] = 0;
       hs[h] = sc[h][0];
       hc[h] = col[h][0];
+      if constexpr (kLdsLists) {
+#pragma unroll
+        for (int i = 1; i < WMAX; ++i) {
+          lsc[h * WMAX + i][tid] = sc[h][i];
+          lcol[h * WMAX + i][tid] = col[h][i];
+        }
+      }
     }
     for (int r = 0; r < K; ++r) {
       // this lane's best head: the first of its tiles holding the maximum
@@ -852,19 +869,31 @@ __device__ __forceinline__ void select_finalize_item(const K2Args& a) {
         for (int h = 1; h < H; ++h) hcol = bh == h ? hc[h] : hcol;
         row_sc[w][r] = M;
         row_j[w][r] = w * V + hcol;
-        // the winning list moves up by one entry (register moves: the lists
-        // are never indexed at run time)
+        if constexpr (kLdsLists) {
+          // the winning list's next entry, read from LDS
 #pragma unroll
-        for (int h = 0; h < H; ++h) {
-          if (bh == h) {
-#pragma unroll
-            for (int i = 0; i + 1 < WMAX; ++i) {
-              sc[h][i] = sc[h][i + 1];
-              col[h][i] = col[h][i + 1];
+          for (int h = 0; h < H; ++h) {
+            if (bh == h) {
+              const int q = ++ph[h];
+              hs[h] = q < WMAX ? lsc[h * WMAX + q][tid] : -kInf;
+              hc[h] = q < WMAX ? lcol[h * WMAX + q][tid] : 0;
             }
-            sc[h][WMAX - 1] = -kInf;
-            hs[h] = sc[h][0];
-            hc[h] = col[h][0];
+          }
+        } else {
+          // the winning list moves up by one entry (register moves: the lists
+          // are never indexed at run time)
+#pragma unroll
+          for (int h = 0; h < H; ++h) {
+            if (bh == h) {
+#pragma unroll
+              for (int i = 0; i + 1 < WMAX; ++i) {
+                sc[h][i] = sc[h][i + 1];
+                col[h][i] = col[h][i + 1];
+              }
+              sc[h][WMAX - 1] = -kInf;
+              hs[h] = sc[h][0];
+              hc[h] = col[h][0];
+            }
           }
         }
       }
@@ -893,17 +922,11 @@ __device__ __forceinline__ void select_finalize_item(const K2Args& a) {
     return;
   }
 
-  // stage B: lane w < W holds row w's list; lane r keeps round r's winner
-  float rs[WMAX];
-  int rj[WMAX];
-#pragma unroll
-  for (int i = 0; i < WMAX; ++i) {
-    const bool in = lane < W && i < K;
-    rs[i] = in ? row_sc[lane < W ? lane : 0][i] : -kInf;
-    rj[i] = in ? row_j[lane < W ? lane : 0][i] : 0;
-  }
-  float hs = rs[0], fs = -kInf;
-  int hj = rj[0], fj = 0;
+  // stage B: lane w < W holds the head of row w's list, which stays in LDS;
+  // lane r keeps round r's winner
+  int pw = 0;
+  float hs = lane < W ? row_sc[lane < W ? lane : 0][0] : -kInf, fs = -kInf;
+  int hj = lane < W ? row_j[lane < W ? lane : 0][0] : 0, fj = 0;
   for (int r = 0; r < K; ++r) {
     const float M = row16_max_f(hs);  // lanes 0..15 hold every row
     const uint64_t holders = __ballot(lane < 16 && hs == M && M > -kInf);
@@ -914,15 +937,10 @@ __device__ __forceinline__ void select_finalize_item(const K2Args& a) {
       fs = M;
       fj = wj;
     }
-    if (lane == l) {  // the winning row's list moves up by one entry
-#pragma unroll
-      for (int i = 0; i + 1 < WMAX; ++i) {
-        rs[i] = rs[i + 1];
-        rj[i] = rj[i + 1];
-      }
-      rs[WMAX - 1] = -kInf;
-      hs = rs[0];
-      hj = rj[0];
+    if (lane == l) {  // the winning row's next entry
+      ++pw;
+      hs = pw < K ? row_sc[lane][pw] : -kInf;
+      hj = pw < K ? row_j[lane][pw] : 0;
     }
   }
   // exact order of the K winners: rank = number of better winners (the empty
