@@ -233,9 +233,9 @@ void launch_k2(const K2Args& a, int wmax, hipStream_t s, const K6Args* paged = n
 }
 
 // ---- K3 dispatch ----------------------------------------------------------
-// one 16-byte word per thread and parent, 256 threads per workgroup: more
-// threads with fewer stores in flight each measured faster than 2, 4 or 8
-// words per thread, and than workgroups of 512 or 1024 threads
+// one 16-byte word per thread and parent, one wave per workgroup
+// (kK3Threads): more threads with fewer stores in flight each measured faster
+// than 2, 4 or 8 words per thread, and smaller workgroups faster than larger
 constexpr int kK3Words = 1;
 // workgroups along a row: the grid's x extent times the workgroup size must
 // stay below 2^32 work-items

@@ -6,14 +6,13 @@
 
 namespace {
 
-constexpr int kThreads = 256;           // workgroup size of K1, K2, K3, K4
+constexpr int kThreads = 256;           // workgroup size of K1, K2, K4
 constexpr int kWaves = kThreads / 64;   // wave64
 constexpr int kMaxBeam = 16;
 constexpr int kMaxGridRows = 65535;     // rows per launch: the grid's y extent
 constexpr int kListCap = 1024;          // LDS candidate list of the top-W
 constexpr int kMergeNE = 8;             // K2 candidates per thread per batch
 constexpr int kPlanStride = 64;         // int32 words per item of the KV plan
-constexpr int kK3Threads = 256;         // threads per KV-reorder workgroup
 constexpr int kMaxPlanesPerLaunch = 128;
 constexpr float kInf = __builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;

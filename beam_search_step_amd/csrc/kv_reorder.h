@@ -9,6 +9,13 @@ namespace {
 // K3: in-place KV reorder
 // ---------------------------------------------------------------------------
 
+// One wave per workgroup. With each step's reorder on a cold cache (20 steps
+// spread over the search, three runs each): 9,888-9,915 beam steps/s at the
+// Llama-3-8B shape against 9,723-9,762 with 128 threads and 9,380-9,574 with
+// 256; at the wide shape (W = 16) 2,153-2,158 against 2,117-2,145 and
+// 2,112-2,134; Transformer-base within noise.
+constexpr int kK3Threads = 64;
+
 struct K3Args {
   char* planes[kMaxPlanesPerLaunch];
   int64_t row_stride;   // bytes
