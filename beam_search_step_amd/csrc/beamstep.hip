@@ -891,7 +891,7 @@ int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len)
   a7.parity = gen_len & 1;
   a7.max_copies = h->B * h->W;
   const int64_t words = (int64_t)(p->bs - 1) * a7.words_per_pos;  // at most bs-1 positions
-  a7.tiles = (int)((words + kThreads - 1) / kThreads);
+  a7.tiles = (int)((words + kK7Threads - 1) / kK7Threads);
   if (a7.tiles > 0) {
     for (int p0 = 0; p0 < pool->n_planes; p0 += kMaxPlanesPerLaunch) {
       const int np = pool->n_planes - p0 < kMaxPlanesPerLaunch ? pool->n_planes - p0
@@ -900,9 +900,9 @@ int bs_kv_paged_reorder(bs_kv_paged* p, const bs_kv_pool* pool, int32_t gen_len)
       a7.groups = (np + kCopyPlanes - 1) / kCopyPlanes;
       for (int i = 0; i < np; ++i) a7.pools[i] = (char*)pool->pools[p0 + i];
       if (word == 16)
-        hipLaunchKernelGGL(k7_paged_copy<16>, dim3(kCopyGrid), dim3(kThreads), 0, h->stream, a7);
+        hipLaunchKernelGGL(k7_paged_copy<16>, dim3(kCopyGrid), dim3(kK7Threads), 0, h->stream, a7);
       else
-        hipLaunchKernelGGL(k7_paged_copy<4>, dim3(kCopyGrid), dim3(kThreads), 0, h->stream, a7);
+        hipLaunchKernelGGL(k7_paged_copy<4>, dim3(kCopyGrid), dim3(kK7Threads), 0, h->stream, a7);
       rc = launch_status();
       if (rc != BS_OK) return rc;
     }

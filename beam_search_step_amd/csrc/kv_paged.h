@@ -187,16 +187,20 @@ struct K7Args {
 // tile, group of kCopyPlanes pools) of the step's list; a thread moves one
 // word of each pool of its unit's group, all loads issued before the first
 // store. The grid is sized so that a workgroup rarely takes more than one
-// unit (1024 measured 11% faster per step than 256 with blocks of 16
-// positions, 18% with blocks of 32; 2048 no faster), since a workgroup's next
-// unit waits for its previous stores. Loads and stores carry the nontemporal
+// unit, since a workgroup's next unit waits for its previous stores (with
+// 256-thread workgroups, 1024 of them measured 11% faster per step than 256
+// with blocks of 16 positions, 18% with blocks of 32; 2048 no faster).
+// Workgroups are one wave, as in the contiguous reorder: 4096 of 64 threads
+// gave 44,867-45,581 beam steps/s against 43,997-44,554 for 1024 of 256 at the
+// Llama-3-8B shape (blocks of 16, three runs each), 2048 of 64 in between. Loads and stores carry the nontemporal
 // hint, as the contiguous reorder's do (every word is read once and written
 // once): 42,588-42,856 beam steps/s against 40,534-40,821 with plain ones at
 // the Llama-3-8B shape (blocks of 16, three runs each).
 constexpr int kCopyPlanes = 8;
-constexpr int kCopyGrid = 1024;
+constexpr int kCopyGrid = 4096;
+constexpr int kK7Threads = 64;
 template <int WORD>
-__global__ __launch_bounds__(kThreads) void k7_paged_copy(K7Args a) {
+__global__ __launch_bounds__(kK7Threads) void k7_paged_copy(K7Args a) {
   using WT = typename Word<WORD>::type;
   const int units = min(a.ncpy[a.parity], a.max_copies) * a.tiles * a.groups;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k7_paged_copy(K7Args a) {
     const int tile = rest / a.groups, grp = rest - tile * a.groups;
     const int* c = a.cpy + (int64_t)f * 3;
     const int src = c[0], dst = c[1], npos = c[2];
-    const int e = tile * kThreads + threadIdx.x;
+    const int e = tile * kK7Threads + threadIdx.x;
     if (e >= npos * a.words_per_pos) continue;
     const int pos = e / a.words_per_pos;
     const int64_t off = pos * a.pos_stride + (int64_t)(e - pos * a.words_per_pos) * WORD;
