@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     BS_OK = 0,
     BS_EINVAL = -1,  /* invalid argument or configuration            */
-    BS_ENOMEM = -2,  /* device allocation failed (bs_create only)    */
+    BS_ENOMEM = -2,  /* device allocation failed (the create calls)  */
     BS_EDEVICE = -3, /* HIP runtime error                            */
     BS_ESTATE = -4   /* call not valid in the handle's current state */
 } bs_status;
