@@ -1055,3 +1055,66 @@ def test_graph_capture_replays_match_eager(dev):
         assert torch.equal(plane, eager_plane), f"replay {rep}: KV differs"
         assert noise.isfinite()
     g.close()
+
+
+def test_two_handles_on_two_streams(dev):
+    """Two searches on HIP streams of their own, their steps and reorders
+    issued alternately with no synchronisation between them, give the bits
+    each gives alone on the null stream: the library keeps no state outside a
+    handle, and every launch of a handle goes to its stream."""
+    import beam_search_step_amd as bs
+    toy = synth.WORKLOADS["toy"]
+    wls = [toy.replace(batch=4, beam=4, vocab=5000, max_steps=12, seed=11),
+           toy.replace(batch=3, beam=8, vocab=3000, max_steps=12, seed=12)]
+    T = 12
+    logits = [[to_device(synth.logits(wl, t), dev) for t in range(1, T + 1)] for wl in wls]
+    words = 4
+
+    def planes_for(wl):
+        rng = np.random.default_rng(wl.seed)
+        return [torch.from_numpy(rng.integers(-2 ** 31, 2 ** 31 - 1, size=(wl.rows, T, words))
+                                 .astype(np.int32)).to(dev) for _ in range(2)]
+
+    def run(order, streams):
+        gs = [bs.BeamSearch.for_workload(wl, stream=s)
+              for wl, s in zip(wls, streams)]
+        kv = [planes_for(wl) for wl in wls]
+        torch.cuda.synchronize()   # the planes' copies ran on the default stream
+        hist = [[] for _ in wls]
+        for t in range(1, T + 1):
+            for i in order:
+                ctx = torch.cuda.stream(streams[i]) if streams[i] is not None else None
+                if ctx:
+                    ctx.__enter__()
+                bi, tk, sc, dn = gs[i].step(logits[i][t - 1])
+                hist[i].append([x.clone() for x in (bi, tk, sc, dn)])
+                gs[i].reorder_kv(kv[i], t)
+                if ctx:
+                    ctx.__exit__(None, None, None)
+        fin = [[] for _ in wls]
+        for i in order:
+            g = gs[i]
+            ctx = torch.cuda.stream(streams[i]) if streams[i] is not None else None
+            if ctx:
+                ctx.__enter__()
+            fin[i] = [x.clone() for x in g.finalize()]
+            if ctx:
+                ctx.__exit__(None, None, None)
+        torch.cuda.synchronize()
+        out = [([[x.cpu().numpy() for x in h] for h in hist[i]], [p.cpu().numpy() for p in kv[i]],
+                [x.cpu().numpy() for x in fin[i]]) for i in range(len(wls))]
+        for g in gs:
+            g.close()
+        return out
+
+    alone = [run([i], [None, None])[i] for i in range(len(wls))]
+    together = run([0, 1], [torch.cuda.Stream(), torch.cuda.Stream()])
+    for i in range(len(wls)):
+        (h_a, kv_a, f_a), (h_t, kv_t, f_t) = alone[i], together[i]
+        for t in range(T):
+            for a, b in zip(h_a[t], h_t[t]):
+                assert np.array_equal(a, b), f"search {i} step {t + 1} differs across streams"
+        for a, b in zip(kv_a, kv_t):
+            assert np.array_equal(a, b), f"search {i}: KV differs across streams"
+        for a, b in zip(f_a, f_t):
+            assert np.array_equal(a, b), f"search {i}: final hypotheses differ across streams"
